@@ -1,0 +1,335 @@
+// C-ABI entry points (include/fp8attn.h): argument validation, split-KV planning, dispatch.
+//
+// Validation runs entirely on host-visible values and finishes before the first HIP call, so
+// every rejection path can be exercised without a GPU.  Rejections for unsupported
+// combinations name the q/k/v dtypes and head sizes, following the gating convention in vLLM
+// PR #60372 (review thread: unsupported calls raise an error naming dtypes and head sizes).
+#include "../../include/fp8attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "params.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+fp8attn_status fail(fp8attn_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+fp8attn_status ok() {
+  g_err.clear();
+  return FP8ATTN_OK;
+}
+
+fp8attn_status hip_fail(const char* where, hipError_t e) {
+  return fail(FP8ATTN_ERR_HIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+}
+
+const char* dtype_name(int32_t t) { return t == FP8ATTN_BF16 ? "bf16" : t == FP8ATTN_E4M3 ? "e4m3" : "unknown"; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Supported (q dtype, head dim) pairs: native FP8 at head dim 256 (vLLM PR #63139, Overview) and
+// BF16 Q at head dim 512 (vLLM PR #60372, Overview), plus head dim 64 for both as a small case.
+bool supported_combo(int32_t q_dtype, int32_t d) {
+  if (q_dtype == FP8ATTN_E4M3) return d == 64 || d == 256;
+  if (q_dtype == FP8ATTN_BF16) return d == 64 || d == 512;
+  return false;
+}
+
+fp8attn_status validate_attn(const char* fn, const fp8attn_attn_args* a, bool decode) {
+  if (!a) return fail(FP8ATTN_ERR_INVALID_ARG, "%s: args is NULL", fn);
+  if (a->q_dtype != FP8ATTN_BF16 && a->q_dtype != FP8ATTN_E4M3)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: unknown q_dtype %d", fn, a->q_dtype);
+  if (a->reserved0 != 0 || a->reserved1 != 0)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: reserved fields must be 0", fn);
+  if (a->num_q_heads <= 0 || a->num_kv_heads <= 0 || a->head_dim <= 0)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: head counts and head_dim must be positive (num_q_heads=%d num_kv_heads=%d head_dim=%d)",
+                fn, a->num_q_heads, a->num_kv_heads, a->head_dim);
+  if (a->num_q_heads % a->num_kv_heads != 0)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: num_q_heads (%d) must be a multiple of num_kv_heads (%d)", fn,
+                a->num_q_heads, a->num_kv_heads);
+  if (!supported_combo(a->q_dtype, a->head_dim))
+    return fail(FP8ATTN_ERR_UNSUPPORTED,
+                "%s: unsupported combination q=%s k=e4m3 v=e4m3 head_size=%d head_size_v=%d "
+                "(supported: q=e4m3 with head_size 64 or 256; q=bf16 with head_size 64 or 512; "
+                "k/v always e4m3 with head_size_v == head_size)",
+                fn, dtype_name(a->q_dtype), a->head_dim, a->head_dim);
+  if (a->causal != 1)
+    return fail(FP8ATTN_ERR_UNSUPPORTED,
+                "%s: non-causal attention is not supported (q=%s k=e4m3 v=e4m3 head_size=%d): only causal "
+                "and sliding-window masks are implemented",
+                fn, dtype_name(a->q_dtype), a->head_dim);
+  if (a->window == 0 || a->window < -1)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: window must be -1 (none) or >= 1, got %d", fn, a->window);
+  if (a->page_size <= 0 || a->page_size % 64 != 0)
+    return fail(FP8ATTN_ERR_UNSUPPORTED,
+                "%s: page_size %d is not a positive multiple of 64 (q=%s k=e4m3 v=e4m3 head_size=%d)", fn,
+                a->page_size, dtype_name(a->q_dtype), a->head_dim);
+  if (a->q_dtype == FP8ATTN_BF16 && a->q_descale != nullptr)
+    return fail(FP8ATTN_ERR_UNSUPPORTED,
+                "%s: q=bf16 takes unquantized queries, so q_descale must be NULL (k=e4m3 v=e4m3 head_size=%d)",
+                fn, a->head_dim);
+  if (a->batch < 0 || a->total_q < 0 || a->max_seqlen_q < 0 || a->max_seqlen_k < 0)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: batch, total_q, max_seqlen_q and max_seqlen_k must be >= 0", fn);
+  if (a->total_q > 0 && a->max_seqlen_q == 0)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: total_q > 0 needs max_seqlen_q > 0", fn);
+  if (a->max_seqlen_q > a->max_seqlen_k && a->total_q > 0)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: max_seqlen_q (%d) exceeds max_seqlen_k (%d): q_len must be <= KV length",
+                fn, a->max_seqlen_q, a->max_seqlen_k);
+  if (decode && a->max_seqlen_q > 16)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: max_seqlen_q %d > 16; use fp8attn_prefill_varlen", fn, a->max_seqlen_q);
+  if (!(a->softmax_scale == a->softmax_scale) || std::isinf(a->softmax_scale))
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: softmax_scale must be finite", fn);
+  if (a->descale_stride_b < 0 || a->descale_stride_h < 0)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: descale strides must be >= 0", fn);
+  if (a->total_q == 0 || a->batch == 0) return ok();
+
+  if (!a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->cu_seqlens_q || !a->seqlens_k || !a->out)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: a required pointer (q, k_cache, v_cache, block_table, cu_seqlens_q, "
+                "seqlens_k, out) is NULL", fn);
+  const int64_t qelt = a->q_dtype == FP8ATTN_BF16 ? 2 : 1;
+  if (!aligned(a->q, 16) || (a->q_stride_tok * qelt) % 16 != 0 || (a->q_stride_head * qelt) % 16 != 0 ||
+      a->q_stride_tok < 0 || a->q_stride_head < 0)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: q must be 16-byte aligned with 16-byte-multiple strides", fn);
+  if (!aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) || a->kv_stride_tok % 16 != 0 ||
+      a->kv_stride_page % 16 != 0 || a->kv_stride_head % 16 != 0 || a->kv_stride_tok < a->head_dim ||
+      a->kv_stride_head < 0 || a->kv_stride_page < 0)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: k/v caches must be 16-byte aligned with 16-byte-multiple strides "
+                "(kv_stride_tok >= head_dim)", fn);
+  if (!aligned(a->out, 16) || (a->out_stride_tok * 2) % 16 != 0 || (a->out_stride_head * 2) % 16 != 0 ||
+      a->out_stride_tok < 0 || a->out_stride_head < 0)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: out must be 16-byte aligned with 16-byte-multiple strides", fn);
+  if (a->lse && !aligned(a->lse, 4)) return fail(FP8ATTN_ERR_INVALID_ARG, "%s: lse must be 4-byte aligned", fn);
+  const int64_t need_pages = (a->max_seqlen_k + a->page_size - 1) / a->page_size;
+  if (a->block_table_stride < need_pages && a->batch > 1)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: block_table_stride %lld is smaller than ceil(max_seqlen_k/page_size) = %lld",
+                fn, (long long)a->block_table_stride, (long long)need_pages);
+  return ok();
+}
+
+fp8attn::AttnParams make_params(const fp8attn_attn_args* a) {
+  fp8attn::AttnParams p{};
+  p.q = a->q;
+  p.q_stride_tok = a->q_stride_tok;
+  p.q_stride_head = a->q_stride_head;
+  p.k_cache = a->k_cache;
+  p.v_cache = a->v_cache;
+  p.kv_stride_page = a->kv_stride_page;
+  p.kv_stride_tok = a->kv_stride_tok;
+  p.kv_stride_head = a->kv_stride_head;
+  p.page_size = a->page_size;
+  p.batch = a->batch;
+  p.block_table = a->block_table;
+  p.bt_stride = a->block_table_stride;
+  p.cu_seqlens_q = a->cu_seqlens_q;
+  p.seqlens_k = a->seqlens_k;
+  p.total_q = a->total_q;
+  p.hq = a->num_q_heads;
+  p.hkv = a->num_kv_heads;
+  p.group = a->num_q_heads / a->num_kv_heads;
+  p.q_descale = a->q_descale;
+  p.k_descale = a->k_descale;
+  p.v_descale = a->v_descale;
+  p.ds_stride_b = a->descale_stride_b;
+  p.ds_stride_h = a->descale_stride_h;
+  const float sc = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt((float)a->head_dim);
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.window = a->window;
+  p.out = a->out;
+  p.out_stride_tok = a->out_stride_tok;
+  p.out_stride_head = a->out_stride_head;
+  p.lse = a->lse;
+  p.max_seqlen_q = a->max_seqlen_q;
+  p.num_splits = 1;
+  return p;
+}
+
+struct DecodePlan {
+  int32_t row_groups;
+  int32_t max_units;
+  int32_t splits;
+  int32_t units_per_split;
+  size_t ws_bytes;
+  int64_t grid;
+};
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Split-KV plan from host-known maxima only (no device reads, so the call is capturable).
+// Automatic mode picks the split count from the work per block, with no fixed cap (vLLM PR
+// #60372, Claims): about 2 MiB of K+V per block, then more splits until the grid holds at
+// least two blocks per compute unit, never fewer than 4 units (64 keys) per split.
+DecodePlan plan_decode(const fp8attn_attn_args* a, int32_t requested) {
+  DecodePlan pl{};
+  const int G = a->num_q_heads / a->num_kv_heads;
+  pl.row_groups = (a->max_seqlen_q * G + 15) / 16;
+  int64_t vis = a->max_seqlen_k;
+  if (a->window >= 1) vis = std::min<int64_t>(vis, (int64_t)a->window + a->max_seqlen_q - 1);
+  pl.max_units = (int32_t)((vis + 15) / 16 + 1);
+  const int64_t items = (int64_t)a->num_kv_heads * a->batch * pl.row_groups;
+  int64_t S;
+  if (requested > 0) {
+    S = requested;
+  } else {
+    const int64_t bytes_per_unit = 16 * 2 * (int64_t)a->head_dim;
+    const int64_t cus = cu_count();
+    int64_t ups = std::max<int64_t>(4, (2 << 20) / bytes_per_unit);
+    S = (pl.max_units + ups - 1) / ups;
+    while (items * S < 2 * (int64_t)cus && (pl.max_units + S) / (S + 1) >= 4) ++S;
+  }
+  S = std::max<int64_t>(1, std::min<int64_t>(S, pl.max_units));
+  pl.units_per_split = (int32_t)((pl.max_units + S - 1) / S);
+  S = (pl.max_units + pl.units_per_split - 1) / pl.units_per_split;
+  pl.splits = (int32_t)S;
+  pl.ws_bytes = 0;
+  if (S > 1) {
+    const size_t rows = (size_t)a->total_q * a->num_q_heads;
+    pl.ws_bytes = round_up(S * rows * a->head_dim * sizeof(float)) + round_up(S * rows * sizeof(float));
+  }
+  pl.grid = items * S;
+  return pl;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fp8attn_version(void) { return 100; }
+
+const char* fp8attn_last_error(void) { return g_err.c_str(); }
+
+fp8attn_status fp8attn_quantize_q(const void* q_bf16, int64_t num_tokens, int32_t num_heads, int32_t head_dim,
+                                  int64_t stride_tok, int64_t stride_head, const float* q_descale,
+                                  void* q_e4m3_out, hipStream_t stream) {
+  const char* fn = "fp8attn_quantize_q";
+  if (num_tokens < 0 || num_heads <= 0 || head_dim <= 0)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: num_tokens >= 0, num_heads > 0 and head_dim > 0 required", fn);
+  if (head_dim % 8 != 0)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: head_dim %d is not a multiple of 8", fn, head_dim);
+  if (stride_tok < 0 || stride_head < 0 || stride_tok % 8 != 0 || stride_head % 8 != 0)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: strides must be non-negative multiples of 8 elements", fn);
+  if (num_tokens == 0) return ok();
+  if (!q_bf16 || !q_e4m3_out) return fail(FP8ATTN_ERR_INVALID_ARG, "%s: q_bf16 and q_e4m3_out must be non-NULL", fn);
+  if (!aligned(q_bf16, 16) || !aligned(q_e4m3_out, 8))
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: q_bf16 must be 16-byte and q_e4m3_out 8-byte aligned", fn);
+  hipError_t e = fp8attn::launch_quantize_q(q_bf16, num_tokens, num_heads, head_dim, stride_tok, stride_head,
+                                            q_descale, q_e4m3_out, stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
+fp8attn_status fp8attn_decode_paged(const fp8attn_attn_args* args, int32_t num_splits, void* workspace,
+                                    size_t workspace_bytes, size_t* workspace_needed, int32_t* num_splits_used,
+                                    hipStream_t stream) {
+  const char* fn = "fp8attn_decode_paged";
+  fp8attn_status st = validate_attn(fn, args, true);
+  if (st != FP8ATTN_OK) return st;
+  if (num_splits < 0) return fail(FP8ATTN_ERR_INVALID_ARG, "%s: num_splits must be >= 0 (0 = automatic)", fn);
+  if (args->total_q == 0 || args->batch == 0) {
+    if (workspace_needed) *workspace_needed = 0;
+    if (num_splits_used) *num_splits_used = 1;
+    return ok();
+  }
+  const DecodePlan pl = plan_decode(args, num_splits);
+  if (workspace_needed) *workspace_needed = pl.ws_bytes;
+  if (num_splits_used) *num_splits_used = pl.splits;
+  if (!workspace && workspace_needed) return ok();  // size query
+  if (pl.grid >= (int64_t)1 << 31)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: grid of %lld blocks is too large", fn, (long long)pl.grid);
+  fp8attn::AttnParams p = make_params(args);
+  p.num_splits = pl.splits;
+  p.units_per_split = pl.units_per_split;
+  p.row_groups = pl.row_groups;
+  if (pl.splits > 1) {
+    if (!workspace || workspace_bytes < pl.ws_bytes)
+      return fail(FP8ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d splits, got %zu", fn,
+                  pl.ws_bytes, pl.splits, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, kAlign))
+      return fail(FP8ATTN_ERR_INVALID_ARG, "%s: workspace must be %zu-byte aligned", fn, kAlign);
+    const size_t rows = (size_t)args->total_q * args->num_q_heads;
+    p.part_o = reinterpret_cast<float*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                          round_up((size_t)pl.splits * rows * args->head_dim * sizeof(float)));
+  }
+  hipError_t e = fp8attn::launch_decode(p, args->q_dtype == FP8ATTN_E4M3, args->head_dim, pl.grid, stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  if (pl.splits > 1) {
+    e = fp8attn::launch_combine(p.part_o, p.part_lse, pl.splits, args->total_q, args->num_q_heads, args->head_dim,
+                                args->out, args->out_stride_tok, args->out_stride_head, args->lse, stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
+  return ok();
+}
+
+fp8attn_status fp8attn_prefill_varlen(const fp8attn_attn_args* args, hipStream_t stream) {
+  const char* fn = "fp8attn_prefill_varlen";
+  fp8attn_status st = validate_attn(fn, args, false);
+  if (st != FP8ATTN_OK) return st;
+  if (args->total_q == 0 || args->batch == 0) return ok();
+  fp8attn::AttnParams p = make_params(args);
+  const int G = args->num_q_heads / args->num_kv_heads;
+  p.row_groups = (args->max_seqlen_q * G + 15) / 16;
+  int64_t vis = args->max_seqlen_k;
+  p.num_splits = 1;
+  p.units_per_split = (int32_t)((vis + 15) / 16 + 1);
+  const int64_t grid = (int64_t)args->num_kv_heads * args->batch * p.row_groups;
+  if (grid >= (int64_t)1 << 31)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: grid of %lld blocks is too large", fn, (long long)grid);
+  hipError_t e = fp8attn::launch_decode(p, args->q_dtype == FP8ATTN_E4M3, args->head_dim, grid, stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
+fp8attn_status fp8attn_splitkv_combine(const float* partial_o, const float* partial_lse, int32_t num_splits,
+                                       int64_t total_q, int32_t num_q_heads, int32_t head_dim, void* out_bf16,
+                                       int64_t out_stride_tok, int64_t out_stride_head, float* lse_out,
+                                       hipStream_t stream) {
+  const char* fn = "fp8attn_splitkv_combine";
+  if (num_splits <= 0 || total_q < 0 || num_q_heads <= 0)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: num_splits > 0, total_q >= 0 and num_q_heads > 0 required", fn);
+  if (head_dim != 64 && head_dim != 256 && head_dim != 512)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 256, 512}", fn, head_dim);
+  if (out_stride_tok < 0 || out_stride_head < 0)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: output strides must be >= 0", fn);
+  if (total_q == 0) return ok();
+  if (!partial_o || !partial_lse || !out_bf16)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: partial_o, partial_lse and out_bf16 must be non-NULL", fn);
+  if (!aligned(partial_o, 16) || !aligned(partial_lse, 4) || !aligned(out_bf16, 2) || (lse_out && !aligned(lse_out, 4)))
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: partial_o must be 16-byte aligned", fn);
+  hipError_t e = fp8attn::launch_combine(partial_o, partial_lse, num_splits, total_q, num_q_heads, head_dim, out_bf16,
+                                         out_stride_tok, out_stride_head, lse_out, stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
+}  // extern "C"

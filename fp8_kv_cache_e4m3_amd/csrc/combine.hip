@@ -1,0 +1,75 @@
+// Log-sum-exp combine of split-KV partials (vLLM PR #60372, Details: the combine work that
+// split-KV adds).  One wave per row (token, q head): M = max_s lse_s, w_s = exp(lse_s - M),
+// o = sum_s w_s o_s / sum_s w_s, lse = M + ln sum_s w_s.  Splits with lse = -inf are skipped
+// (their partials are never read).  Each lane owns D/64 contiguous values of the row.
+#include "device.h"
+#include "params.h"
+
+namespace fp8attn {
+
+template <int D>
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_lse, int32_t S,
+                                                      int64_t rows, int32_t hq, __bf16* __restrict__ out,
+                                                      int64_t out_stride_tok, int64_t out_stride_head,
+                                                      float* __restrict__ lse_out) {
+  constexpr int PL = D / 64;  // values per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= rows) return;
+  float M = kNegInf;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, part_lse[(int64_t)s * rows + n]);
+  float acc[PL];
+#pragma unroll
+  for (int c = 0; c < PL; ++c) acc[c] = 0.f;
+  float wsum = 0.f;
+  if (M != kNegInf) {
+    for (int s = 0; s < S; ++s) {
+      const float l = part_lse[(int64_t)s * rows + n];
+      if (l == kNegInf) continue;
+      const float w = __expf(l - M);
+      wsum += w;
+      const float* src = part_o + ((int64_t)s * rows + n) * D + lane * PL;
+      if constexpr (PL == 8) {
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(src);
+        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(src + 4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) { acc[c] += w * a[c]; acc[4 + c] += w * b[c]; }
+      } else if constexpr (PL == 4) {
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(src);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] += w * a[c];
+      } else {
+#pragma unroll
+        for (int c = 0; c < PL; ++c) acc[c] += w * src[c];
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  const int64_t tok = n / hq, hh = n % hq;
+  __bf16* dst = out + tok * out_stride_tok + hh * out_stride_head + lane * PL;
+#pragma unroll
+  for (int c = 0; c < PL; ++c) dst[c] = (__bf16)(acc[c] * inv);
+  if (lse_out && lane == 0) lse_out[n] = wsum > 0.f ? M + __logf(wsum) : kNegInf;
+}
+
+hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t S, int64_t total_q,
+                          int32_t hq, int32_t d, void* out, int64_t out_stride_tok,
+                          int64_t out_stride_head, float* lse_out, hipStream_t stream) {
+  const int64_t rows = total_q * hq;
+  if (rows == 0) return hipSuccess;
+  const dim3 g((unsigned)((rows + 3) / 4)), blk(256);
+  __bf16* o = reinterpret_cast<__bf16*>(out);
+  if (d == 512)
+    hipLaunchKernelGGL(combine_kernel<512>, g, blk, 0, stream, part_o, part_lse, S, rows, hq, o,
+                       out_stride_tok, out_stride_head, lse_out);
+  else if (d == 256)
+    hipLaunchKernelGGL(combine_kernel<256>, g, blk, 0, stream, part_o, part_lse, S, rows, hq, o,
+                       out_stride_tok, out_stride_head, lse_out);
+  else
+    hipLaunchKernelGGL(combine_kernel<64>, g, blk, 0, stream, part_o, part_lse, S, rows, hq, o,
+                       out_stride_tok, out_stride_head, lse_out);
+  return hipGetLastError();
+}
+
+}  // namespace fp8attn

@@ -1,0 +1,339 @@
+// Split-KV paged attention for a few query tokens per sequence (decode, spec-decode verify).
+//
+// What it computes: masked softmax attention of one 16-row query tile (rows = (token, q head)
+// pairs of one kv head, token-major) over the keys of one KV split, on a paged E4M3 cache with
+// per-tensor descales (vLLM PR #60372, Overview/Claims; prhub digest of vLLM PR #48666, Key
+// code), for both variants:
+//   QFP8 = true : E4M3 Q codes (vLLM PR #63139, Overview), QK^T on the FP8 MFMA;
+//   QFP8 = false: BF16 Q, K dequantized in registers (exact: E4M3 values are bf16 values),
+//                 QK^T on the BF16 MFMA.
+// PV runs on the BF16 MFMA in both variants: V bytes are dequantized exactly to bf16 and P is
+// rounded once to bf16.  Decode is HBM-bound, so the cheaper FP8 PV would not move the time but
+// would cost accuracy on short rows.
+//
+// Design (gfx950, wave64):
+//  * Work item = (kv head, split, sequence, row tile), XCD-aware block order.  4 waves per
+//    block; each wave streams its own 16-key units (a quarter of the split) straight from HBM
+//    into registers, with the next unit's loads in flight while the current one is computed.
+//    No LDS staging and no barriers in the main loop.
+//  * S^T = K * Q^T: the 16 keys are MFMA rows, the 16 query rows are MFMA columns, so every
+//    query row lives on one lane column (lane % 16) and its softmax state is per lane.
+//  * O^T = V^T * P^T: P^T comes straight out of the S^T accumulator layout (lane (r, g) holds
+//    keys 4g..4g+3 of row r), which is the B operand of the 16x16x16 BF16 MFMA.  V^T operands
+//    come from 4 keys x 16 bytes per lane via a byte transpose (v_perm) and an exact convert.
+//  * The 4 waves' (max, sum, O) are merged through LDS at the end; one split writes bf16 O and
+//    LSE directly, several splits write fp32 partials for the LSE combine.
+#include "device.h"
+#include "params.h"
+
+namespace fp8attn {
+
+template <int D>
+struct DecodeShape {
+  static constexpr int kKeys = 16;                    // keys per unit
+  static constexpr int KCH = D / 64;                  // 16-byte K chunks per lane per unit
+  static constexpr int CW = D >= 256 ? 16 : D / 16;   // V bytes per lane per key per block
+  static constexpr int VBLK = D / (16 * CW);          // V column blocks
+  static constexpr int NT = D / 16;                   // O^T tiles (16 d-rows each)
+  static constexpr int RS = D + 4;                    // LDS row stride (floats), padded
+  static_assert(D == 64 || D == 256 || D == 512, "head dim");
+};
+
+template <int D>
+struct UnitRegs {
+  u32x4_t k[DecodeShape<D>::KCH];
+  uint32_t v[4][DecodeShape<D>::VBLK][DecodeShape<D>::CW / 4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_unit(UnitRegs<D>& ur, const uint8_t* __restrict__ kpage,
+                                          const uint8_t* __restrict__ vpage, int64_t sT, int slot0,
+                                          int col, int grp) {
+  using S = DecodeShape<D>;
+  const uint8_t* kp = kpage + (int64_t)(slot0 + col) * sT + 16 * grp;
+#pragma unroll
+  for (int c = 0; c < S::KCH; ++c) ur.k[c] = *reinterpret_cast<const u32x4_t*>(kp + 64 * c);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint8_t* vp = vpage + (int64_t)(slot0 + 4 * grp + i) * sT + col * S::CW;
+#pragma unroll
+    for (int blk = 0; blk < S::VBLK; ++blk) {
+      if constexpr (S::CW == 16) {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(vp + blk * 16 * S::CW);
+        ur.v[i][blk][0] = w[0];
+        ur.v[i][blk][1] = w[1];
+        ur.v[i][blk][2] = w[2];
+        ur.v[i][blk][3] = w[3];
+      } else {
+        ur.v[i][blk][0] = *reinterpret_cast<const uint32_t*>(vp + blk * 16 * S::CW);
+      }
+    }
+  }
+}
+
+template <bool QFP8, int D>
+struct QRegs;
+template <int D>
+struct QRegs<true, D> { uint64_t q[2 * DecodeShape<D>::KCH]; };
+template <int D>
+struct QRegs<false, D> { bf16x8_t q[2 * DecodeShape<D>::KCH]; };
+
+template <bool QFP8, int D>
+__global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
+  using S = DecodeShape<D>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+
+  // ---- work item -------------------------------------------------------------------------
+  int64_t id = xcd_remap(blockIdx.x, gridDim.x);
+  const int rt = (int)(id % p.row_groups); id /= p.row_groups;
+  const int b = (int)(id % p.batch); id /= p.batch;
+  const int s = (int)(id % p.num_splits); id /= p.num_splits;
+  const int h = (int)id;
+  const int G = p.group;
+
+  const int t0 = p.cu_seqlens_q[b];
+  const int ql = p.cu_seqlens_q[b + 1] - t0;
+  const int L = p.seqlens_k[b];
+  const int nrows = ql * G;
+  const int row0 = rt * 16;
+  if (row0 >= nrows) return;
+  const int rlast = min(row0 + 16, nrows) - 1;
+  const int p_first = L - ql + row0 / G;
+  const int p_last = L - ql + rlast / G;
+  const int W = p.window;
+  const int k_lo = W >= 1 ? max(0, p_first - W + 1) : 0;
+  const int u_begin = k_lo / 16;
+  const int u_end = (p_last + 16) / 16;              // ceil((p_last + 1) / 16)
+  const int su0 = u_begin + s * p.units_per_split;
+  const int su1 = min(u_end, su0 + p.units_per_split);
+  // keys every row of this tile can see: [full_lo, p_first]
+  const int full_lo = W >= 1 ? p_last - W + 1 : 0;
+
+  // this lane's query row
+  const int r = row0 + col;
+  const bool rvalid = r < nrows;
+  const int tok = rvalid ? r / G : rlast / G;
+  const int hq = h * G + (rvalid ? r % G : rlast % G);
+  const int pos = L - ql + tok;
+
+  if (su0 >= su1) {  // nothing visible in this split: neutral partial for the combine
+    if (p.num_splits > 1 && threadIdx.x < 16 && rvalid)
+      p.part_lse[((int64_t)s * p.total_q + t0 + tok) * p.hq + hq] = kNegInf;
+    return;
+  }
+
+  const float kd = p.k_descale ? p.k_descale[b * p.ds_stride_b + h * p.ds_stride_h] : 1.0f;
+  const float vd = p.v_descale ? p.v_descale[b * p.ds_stride_b + h * p.ds_stride_h] : 1.0f;
+  float cscale = p.scale_log2 * kd;
+  if constexpr (QFP8) cscale *= p.q_descale ? p.q_descale[0] : 1.0f;
+
+  // ---- Q^T operand (rows on lane columns) ---------------------------------------------------
+  QRegs<QFP8, D> qr;
+  {
+    if constexpr (QFP8) {
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)(t0 + tok) * p.q_stride_tok +
+                          (int64_t)hq * p.q_stride_head + 16 * grp;
+#pragma unroll
+      for (int c = 0; c < S::KCH; ++c) {
+        u32x4_t w = rvalid ? *reinterpret_cast<const u32x4_t*>(qp + 64 * c) : u32x4_t{0, 0, 0, 0};
+        qr.q[2 * c] = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
+        qr.q[2 * c + 1] = (uint64_t)w[2] | ((uint64_t)w[3] << 32);
+      }
+    } else {
+      const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)(t0 + tok) * p.q_stride_tok +
+                         (int64_t)hq * p.q_stride_head + 16 * grp;
+#pragma unroll
+      for (int c = 0; c < S::KCH; ++c) {
+        const bf16x8_t z = {};
+        qr.q[2 * c] = rvalid ? *reinterpret_cast<const bf16x8_t*>(qp + 64 * c) : z;
+        qr.q[2 * c + 1] = rvalid ? *reinterpret_cast<const bf16x8_t*>(qp + 64 * c + 8) : z;
+      }
+    }
+  }
+
+  f32x4_t oacc[S::NT];
+#pragma unroll
+  for (int t = 0; t < S::NT; ++t) oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.f;
+
+  const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
+  const uint8_t* kbase = p.k_cache + (int64_t)h * p.kv_stride_head;
+  const uint8_t* vbase = p.v_cache + (int64_t)h * p.kv_stride_head;
+  const int64_t sT = p.kv_stride_tok, sP = p.kv_stride_page;
+  const int ps = p.page_size;
+
+  auto issue = [&](UnitRegs<D>& ur, int u) {
+    const int j0 = u * 16;
+    const int64_t page = bt[j0 / ps];
+    const int slot0 = j0 % ps;
+    load_unit<D>(ur, kbase + page * sP, vbase + page * sP, sT, slot0, col, grp);
+  };
+
+  auto compute = [&](const UnitRegs<D>& ur, int u) {
+    // S^T tile: rows = 16 keys of the unit, columns = 16 query rows
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < S::KCH; ++c) {
+      if constexpr (QFP8) {
+        const uint64_t k0 = (uint64_t)ur.k[c][0] | ((uint64_t)ur.k[c][1] << 32);
+        const uint64_t k1 = (uint64_t)ur.k[c][2] | ((uint64_t)ur.k[c][3] << 32);
+        sacc = mfma_fp8_16x16x32(k0, qr.q[2 * c], sacc);
+        sacc = mfma_fp8_16x16x32(k1, qr.q[2 * c + 1], sacc);
+      } else {
+        sacc = mfma_bf16_16x16x32(e4m3x8_to_bf16(ur.k[c][0], ur.k[c][1]), qr.q[2 * c], sacc);
+        sacc = mfma_bf16_16x16x32(e4m3x8_to_bf16(ur.k[c][2], ur.k[c][3]), qr.q[2 * c + 1], sacc);
+      }
+    }
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = sacc[i] * cscale;
+    const int j0 = u * 16;
+    if (!(j0 >= full_lo && j0 + 15 <= p_first)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + 4 * grp + i;
+        const bool vis = j <= pos && (W < 1 || j > pos - W);
+        sv[i] = vis ? sv[i] : kNegInf;
+      }
+    }
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = max_over_groups(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(sv[i] - m_use);
+    l_run = l_run * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
+    m_run = m_new;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int t = 0; t < S::NT; ++t) oacc[t] *= alpha;
+    }
+    const bf16x4_t pb = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
+    // O^T += V^T * P^T
+#pragma unroll
+    for (int blk = 0; blk < S::VBLK; ++blk) {
+#pragma unroll
+      for (int w = 0; w < S::CW / 4; ++w) {
+        uint32_t tr[4];
+        transpose4x4_u8(ur.v[0][blk][w], ur.v[1][blk][w], ur.v[2][blk][w], ur.v[3][blk][w],
+                        tr[0], tr[1], tr[2], tr[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = blk * S::CW + 4 * w + e;
+          oacc[t] = mfma_bf16_16x16x16(e4m3x4_to_bf16(tr[e]), pb, oacc[t]);
+        }
+      }
+    }
+  };
+
+  // ---- main loop: this wave takes units su0+wave, su0+wave+4, ... --------------------------
+  {
+    UnitRegs<D> bufA, bufB;
+    int u = su0 + wave;
+    if (u < su1) issue(bufA, u);
+    if (u + 4 < su1) issue(bufB, u + 4);
+    for (; u < su1; u += 8) {
+      compute(bufA, u);
+      if (u + 8 < su1) issue(bufA, u + 8);
+      if (u + 4 < su1) {
+        compute(bufB, u + 4);
+        if (u + 12 < su1) issue(bufB, u + 12);
+      }
+    }
+  }
+  l_run = sum_over_groups(l_run);
+
+  // ---- merge the 4 waves through LDS --------------------------------------------------------
+  __shared__ float sm_m[4][16];
+  __shared__ float sm_l[4][16];
+  __shared__ float sm_o[4][16][S::RS];
+  if (grp == 0) {
+    sm_m[wave][col] = m_run;
+    sm_l[wave][col] = l_run;
+  }
+  __syncthreads();
+  {
+    float M = fmaxf(fmaxf(sm_m[0][col], sm_m[1][col]), fmaxf(sm_m[2][col], sm_m[3][col]));
+    const float sc = M == kNegInf ? 0.f : fast_exp2(m_run - M);
+    float* orow = &sm_o[wave][col][0];
+#pragma unroll
+    for (int blk = 0; blk < S::VBLK; ++blk) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int e4 = 0; e4 < S::CW / 4; ++e4) {
+          const int t = blk * S::CW + 4 * e4;
+          const f32x4_t v = {oacc[t][i] * sc, oacc[t + 1][i] * sc, oacc[t + 2][i] * sc, oacc[t + 3][i] * sc};
+          *reinterpret_cast<f32x4_t*>(orow + blk * 16 * S::CW + (4 * grp + i) * S::CW + 4 * e4) = v;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- final: thread -> (row, d-part) -------------------------------------------------------
+  {
+    const int row = threadIdx.x & 15;
+    const int part = threadIdx.x >> 4;                 // 16 parts of D/16 values
+    constexpr int PW = D / 16;
+    const int rr = row0 + row;
+    if (rr < nrows) {
+      float mw[4], M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) { mw[w] = sm_m[w][row]; M = fmaxf(M, mw[w]); }
+      float Ls = 0.f;
+      if (M != kNegInf) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) Ls += sm_l[w][row] * fast_exp2(mw[w] - M);
+      }
+      const int tk = t0 + rr / G;
+      const int hh = h * G + rr % G;
+      const float inv = Ls > 0.f ? vd / Ls : 0.f;
+      const float lse2 = Ls > 0.f ? (M + fast_log2(Ls)) : kNegInf;
+      if (p.num_splits == 1) {
+        __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)tk * p.out_stride_tok +
+                     (int64_t)hh * p.out_stride_head + part * PW;
+#pragma unroll
+        for (int c = 0; c < PW; c += 4) {
+          f32x4_t a = *reinterpret_cast<const f32x4_t*>(&sm_o[0][row][part * PW + c]);
+#pragma unroll
+          for (int w = 1; w < 4; ++w) a += *reinterpret_cast<const f32x4_t*>(&sm_o[w][row][part * PW + c]);
+          a *= inv;
+          const bf16x4_t o = {(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3]};
+          *reinterpret_cast<bf16x4_t*>(op + c) = o;
+        }
+        if (p.lse && part == 0) p.lse[(int64_t)tk * p.hq + hh] = lse2 * kLn2;
+      } else {
+        float* op = p.part_o + (((int64_t)s * p.total_q + tk) * p.hq + hh) * D + part * PW;
+#pragma unroll
+        for (int c = 0; c < PW; c += 4) {
+          f32x4_t a = *reinterpret_cast<const f32x4_t*>(&sm_o[0][row][part * PW + c]);
+#pragma unroll
+          for (int w = 1; w < 4; ++w) a += *reinterpret_cast<const f32x4_t*>(&sm_o[w][row][part * PW + c]);
+          *reinterpret_cast<f32x4_t*>(op + c) = a * inv;
+        }
+        if (part == 0) p.part_lse[((int64_t)s * p.total_q + tk) * p.hq + hh] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
+      }
+    }
+  }
+}
+
+hipError_t launch_decode(const AttnParams& p, bool q_e4m3, int head_dim, int64_t grid,
+                         hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  const dim3 g((unsigned)grid), blk(256);
+  if (q_e4m3) {
+    if (head_dim == 256) hipLaunchKernelGGL((decode_kernel<true, 256>), g, blk, 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel<true, 64>), g, blk, 0, stream, p);
+  } else {
+    if (head_dim == 512) hipLaunchKernelGGL((decode_kernel<false, 512>), g, blk, 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel<false, 64>), g, blk, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp8attn

@@ -1,0 +1,128 @@
+// Device helpers for gfx950 (CDNA4): vector types, E4M3 conversions, MFMA wrappers,
+// wave-level reductions and the XCD-aware block remap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace fp8attn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------------------------
+// E4M3 -> bf16, exact: every E4M3 value is a bf16 value.  gfx950's v_cvt_scalef32_pk_bf16_fp8
+// converts two OCP E4M3 bytes (bytes 0,1 or 2,3 of the dword) with a unit scale.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ bf16x2_t e4m3x2_lo_to_bf16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+}
+__device__ __forceinline__ bf16x2_t e4m3x2_hi_to_bf16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+}
+// 8 E4M3 bytes (two dwords) -> 8 bf16 in byte order
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  bf16x2_t a = e4m3x2_lo_to_bf16(w0), b = e4m3x2_hi_to_bf16(w0);
+  bf16x2_t c = e4m3x2_lo_to_bf16(w1), d = e4m3x2_hi_to_bf16(w1);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+// 4 E4M3 bytes (one dword) -> 4 bf16 in byte order
+__device__ __forceinline__ bf16x4_t e4m3x4_to_bf16(uint32_t w) {
+  bf16x2_t a = e4m3x2_lo_to_bf16(w), b = e4m3x2_hi_to_bf16(w);
+  return bf16x4_t{a[0], a[1], b[0], b[1]};
+}
+
+// ---------------------------------------------------------------------------------------------
+// 4x4 byte transpose: in row k holds bytes x[k][0..3]; out e holds x[0..3][e].
+// Written with shifts and masks; the compiler turns them into v_perm_b32.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void transpose4x4_u8(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                                uint32_t& t0, uint32_t& t1, uint32_t& t2, uint32_t& t3) {
+  // interleave bytes of (a0,a1) and (a2,a3)
+  const uint32_t p01l = (a0 & 0xffu) | ((a1 & 0xffu) << 8) | ((a0 & 0xff00u) << 8) | ((a1 & 0xff00u) << 16);
+  const uint32_t p01h = ((a0 >> 16) & 0xffu) | (((a1 >> 16) & 0xffu) << 8) | ((a0 >> 24) << 16) | ((a1 >> 24) << 24);
+  const uint32_t p23l = (a2 & 0xffu) | ((a3 & 0xffu) << 8) | ((a2 & 0xff00u) << 8) | ((a3 & 0xff00u) << 16);
+  const uint32_t p23h = ((a2 >> 16) & 0xffu) | (((a3 >> 16) & 0xffu) << 8) | ((a2 >> 24) << 16) | ((a3 >> 24) << 24);
+  t0 = (p01l & 0xffffu) | (p23l << 16);
+  t1 = (p01l >> 16) | (p23l & 0xffff0000u);
+  t2 = (p01h & 0xffffu) | (p23h << 16);
+  t3 = (p01h >> 16) | (p23h & 0xffff0000u);
+}
+
+// ---------------------------------------------------------------------------------------------
+// fp32 -> E4M3 code, round to nearest even, saturating at +-448, NaN -> 0x7F | sign.
+// Normal range: round the fp32 mantissa to 3 bits with the usual add-half-minus-one plus LSB
+// trick, then rebias the exponent (127 -> 7).  Below 2^-6 (E4M3 subnormals) scale by 2^9,
+// which is exact, and round to an integer 0..8 (8 is the smallest normal, code 0x08).
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu | sign;           // NaN
+  if (a >= 0x43e00000u) return 0x7eu | sign;          // |y| >= 448 (and inf)
+  if (a < 0x3c800000u) {                              // |y| < 2^-6
+    const float f = __uint_as_float(a) * 512.0f;
+    return (uint32_t)__builtin_rintf(f) | sign;
+  }
+  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+  return (r - (120u << 3)) | sign;
+}
+
+// ---------------------------------------------------------------------------------------------
+// MFMA wrappers (operand layouts measured on gfx950):
+//  16x16x32 bf16 / fp8 : lane l supplies row (A) or column (B) l%16 and 8 k-values for k-group
+//                        l/16; C lane l holds rows 4*(l/16)+i, column l%16.
+//  16x16x16 bf16       : same with 4 k-values per lane.
+// A and B use the same (lane group, slot) -> k assignment, so any consistent mapping of the
+// contraction index onto slots is valid.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ f32x4_t mfma_bf16_16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_bf16_16x16x16(bf16x4_t a, bf16x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_fp8_16x16x32(uint64_t a, uint64_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)a, (long)b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Cross-lane helpers (wave64)
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+// reduce over the four 16-lane groups (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float max_over_groups(float v) {
+  v = fmaxf(v, shfl_xor_f(v, 16));
+  return fmaxf(v, shfl_xor_f(v, 32));
+}
+__device__ __forceinline__ float sum_over_groups(float v) {
+  v += shfl_xor_f(v, 16);
+  return v + shfl_xor_f(v, 32);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---------------------------------------------------------------------------------------------
+// XCD-aware remap: the dispatcher sends block i to XCD i % 8.  Give each XCD a contiguous
+// range of logical ids so that neighbouring work items (which share K/V pages) share an L2.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t n) {
+  constexpr int64_t kXcd = 8;
+  const int64_t per = n / kXcd, rem = n % kXcd;
+  const int64_t x = bid % kXcd, k = bid / kXcd;
+  return x * per + (x < rem ? x : rem) + k;
+}
+
+}  // namespace fp8attn

@@ -1,0 +1,55 @@
+// Internal launch parameters shared by the host layer (api.cpp) and the HIP kernels.
+// Not part of the public ABI (include/fp8attn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace fp8attn {
+
+// Everything one attention kernel launch needs, passed by value as the kernel argument.
+struct AttnParams {
+  const void* q;
+  int64_t q_stride_tok, q_stride_head;        // elements
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  int64_t kv_stride_page, kv_stride_tok, kv_stride_head;  // bytes
+  int32_t page_size;
+  int32_t batch;
+  const int32_t* block_table;
+  int64_t bt_stride;
+  const int32_t* cu_seqlens_q;
+  const int32_t* seqlens_k;
+  int32_t total_q;
+  int32_t hq, hkv, group;                      // group = hq / hkv
+  const float* q_descale;                      // NULL -> 1
+  const float* k_descale;
+  const float* v_descale;
+  int64_t ds_stride_b, ds_stride_h;
+  float scale_log2;                            // softmax_scale * log2(e)
+  int32_t window;                              // -1 or >= 1
+  void* out;                                   // bf16
+  int64_t out_stride_tok, out_stride_head;     // elements
+  float* lse;                                  // optional, [total_q, hq]
+  // split-KV decode
+  int32_t num_splits;                          // S >= 1
+  int32_t units_per_split;                     // 16-key units per split
+  int32_t row_groups;                          // 16-row tiles per (sequence, kv head)
+  int32_t max_seqlen_q;
+  float* part_o;                               // fp32 [S, total_q, hq, d] when S > 1
+  float* part_lse;                             // fp32 [S, total_q, hq]
+};
+
+hipError_t launch_quantize_q(const void* q, int64_t ntok, int32_t nheads, int32_t d,
+                             int64_t stride_tok, int64_t stride_head, const float* q_descale,
+                             void* out, hipStream_t stream);
+
+// Split-KV paged attention over 16-row query tiles.  grid = row_groups * batch * S * hkv.
+hipError_t launch_decode(const AttnParams& p, bool q_e4m3, int head_dim, int64_t grid,
+                         hipStream_t stream);
+
+hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t S, int64_t total_q,
+                          int32_t hq, int32_t d, void* out, int64_t out_stride_tok,
+                          int64_t out_stride_head, float* lse_out, hipStream_t stream);
+
+}  // namespace fp8attn

@@ -160,7 +160,8 @@ def combine_splits(partial_o, partial_lse):
     partial_o [S, n, d] holds each split's normalized output, partial_lse [S, n]
     its LSE (-inf for a split that saw no key).  M = max_s lse_s,
     w_s = exp(lse_s - M), o = sum_s w_s o_s / sum_s w_s and lse = M + ln sum_s w_s.
-    A split with lse = -inf has weight 0 and its o is never read."""
+    A split with lse = -inf has weight 0 and its o is never read.  A row where every split is
+    -inf (no visible key at all) has no softmax: it gets o = 0 and lse = -inf."""
     po = np.asarray(_np(partial_o), dtype=np.float64)
     pl = np.asarray(_np(partial_lse), dtype=np.float64)
     M = pl.max(axis=0)                                   # [n]
@@ -168,8 +169,10 @@ def combine_splits(partial_o, partial_lse):
     w = np.where(fin, np.exp(np.where(fin, pl, 0.0) - np.where(np.isfinite(M), M, 0.0)), 0.0)
     wsum = w.sum(axis=0)
     num = np.einsum("sn,snd->nd", w, np.where(fin[..., None], po, 0.0))
-    o = num / wsum[:, None]
-    return o, M + np.log(wsum)
+    seen = wsum > 0
+    # a row that no split saw has no softmax; it gets o = 0 and lse = -inf
+    o = np.where(seen[:, None], num / np.where(seen, wsum, 1.0)[:, None], 0.0)
+    return o, np.where(seen, M + np.log(np.where(seen, wsum, 1.0)), -np.inf)
 
 
 def split_attention(q_vals, k_pool, v_pool, block_table, cu_seqlens_q, seqlens_k,

@@ -204,6 +204,11 @@ def test_combine_closed_forms():
     oc, lc = combine_splits(o2, l2)
     oe, le = combine_splits(o[[0, 2]], l[[0, 2]])
     assert np.max(np.abs(oc - oe)) < 1e-14 and np.max(np.abs(lc - le)) < 1e-14
+    # a row no split saw: o = 0, lse = -inf
+    l3 = l.copy()
+    l3[:, 2] = -np.inf
+    oc, lc = combine_splits(o, l3)
+    assert np.all(oc[2] == 0) and np.isneginf(lc[2]) and np.isfinite(oc).all()
     # equal lse: plain mean, lse + ln S
     oc, lc = combine_splits(o, np.zeros((3, 5)))
     assert np.max(np.abs(oc - o.mean(axis=0))) < 1e-14 and np.max(np.abs(lc - math.log(3))) < 1e-14

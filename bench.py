@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged FP8-KV attention path on one MI355X.
+
+Main line: the sliding-window decode workload (batch 32, one query token each, KV lengths
+uniform in [1024, 8192], 32 q / 16 kv heads, head dim 256, window 1024, E4M3 Q/K/V).  One step
+is the whole hot path over one batch: quantize Q to E4M3, then split-KV paged attention (plus
+the LSE combine when more than one split is chosen).  ``value`` is the algorithmic KV-read rate:
+bytes of the visible keys and values plus Q read and O written, divided by the step time.
+Four independently drawn input sets rotate so that the working set exceeds the 256 MiB MALL.
+
+``roofline`` covers the attention kernel alone, timed with HIP events on the stream it runs on.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.  ``extra``
+reports the other workload shapes (full-attention decode, spec-verify with a shared prefix,
+sliding-window prefill) with their own roofline fractions.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--profile-pass]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode KV-read GB/s + prefill attention TFLOP/s, % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # dense FP8 MFMA
+BF16_PEAK_TFLOPS = 2500.0      # dense BF16 MFMA
+KERNEL_SOURCES = ["fp8_kv_cache_e4m3_amd/csrc/decode.hip", "fp8_kv_cache_e4m3_amd/csrc/device.h",
+                  "fp8_kv_cache_e4m3_amd/csrc/prefill.hip"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        fp = os.path.join(ROOT, p)
+        if os.path.exists(fp):
+            h.update(open(fp, "rb").read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------------------------------
+# algorithmic work of a workload (visible keys only)
+# ------------------------------------------------------------------------------------------
+def visible_pairs(w):
+    """Number of visible (query token, key) pairs per q head, summed over the batch."""
+    total = 0
+    for L, ql in zip(w.seqlens_k_host, w.q_lens_host):
+        for i in range(ql):
+            p = L - ql + i
+            n = p + 1 if w.window < 1 else min(p + 1, w.window)
+            total += n
+    return total
+
+
+def visible_keys(w):
+    """Keys that at least one query of each sequence sees (the KV bytes any kernel must read)."""
+    total = 0
+    for L, ql in zip(w.seqlens_k_host, w.q_lens_host):
+        lo = 0 if w.window < 1 else max(0, L - ql - w.window + 1)
+        total += L - lo
+    return total
+
+
+def algo_bytes(w):
+    kv = visible_keys(w) * w.num_kv_heads * w.head_dim * 2          # K and V, 1 byte each
+    qb = w.total_q * w.num_q_heads * w.head_dim * (1 if w.q_dtype == "e4m3" else 2)
+    ob = w.total_q * w.num_q_heads * w.head_dim * 2
+    return kv + qb + ob, kv
+
+
+def algo_flops(w):
+    return 4.0 * w.head_dim * visible_pairs(w) * w.num_q_heads
+
+
+# ------------------------------------------------------------------------------------------
+# GPU steps
+# ------------------------------------------------------------------------------------------
+class Runner:
+    def __init__(self, w, entry):
+        import torch
+        import fp8_kv_cache_e4m3_amd as fa
+        self.fa, self.torch, self.w, self.entry = fa, torch, w, entry
+        self.out = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty((w.total_q, w.num_q_heads), dtype=torch.float32, device="cuda")
+        self.qcodes = None
+        if w.q_dtype == "e4m3":
+            self.qcodes = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=torch.uint8, device="cuda")
+        q = self.qcodes if w.q_dtype == "e4m3" else w.q
+        self.args = fa.make_args(q, w.k_pool, w.v_pool, w.block_table, w.cu_seqlens_q, w.seqlens_k,
+                                 w.max_seqlen_q, w.max_seqlen_k, w.q_descale, w.k_descale, w.v_descale,
+                                 0.0, w.window, True, self.out, self.lse)
+        self.ws = None
+        self.splits = 1
+        if entry == "decode":
+            need, self.splits = fa.decode_workspace_size(self.args, 0)
+            if need:
+                self.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def quantize(self, stream):
+        w = self.w
+        if self.qcodes is not None:
+            st = self.fa.LIB.fp8attn_quantize_q(w.q.data_ptr(), w.total_q, w.num_q_heads, w.head_dim,
+                                                w.q.stride(0), w.q.stride(1), w.q_descale.data_ptr(),
+                                                self.qcodes.data_ptr(), stream)
+            assert st == 0, self.fa.fp8attn_last_error()
+
+    def attend(self, stream):
+        import ctypes
+        fa = self.fa
+        if self.entry == "decode":
+            ws = self.ws
+            st = fa.LIB.fp8attn_decode_paged(ctypes.byref(self.args), 0, None if ws is None else ws.data_ptr(),
+                                             0 if ws is None else ws.numel(), None, None, stream)
+        else:
+            st = fa.LIB.fp8attn_prefill_varlen(ctypes.byref(self.args), stream)
+        assert st == 0, fa.fp8attn_last_error()
+
+
+def time_workload(make, entry, nsets, steps, warmup, label):
+    """Returns dict with ms_per_step (whole step) and kernel_ms (attention call only, HIP events)."""
+    import torch
+    t0 = time.time()
+    runners = [Runner(make(seed), entry) for seed in range(nsets)]
+    torch.cuda.synchronize()
+    log(f"[bench] {label}: {nsets} input sets ready in {time.time() - t0:.1f}s; splits={runners[0].splits}")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    for i in range(warmup):
+        r = runners[i % nsets]
+        r.quantize(sh)
+        r.attend(sh)
+    torch.cuda.synchronize()
+    # whole-step timing
+    t0 = time.perf_counter()
+    for i in range(steps):
+        r = runners[i % nsets]
+        r.quantize(sh)
+        r.attend(sh)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    # attention-kernel timing with events on the launch stream
+    evs = []
+    for i in range(steps):
+        r = runners[i % nsets]
+        r.quantize(sh)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        r.attend(sh)
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    kms = sorted(a.elapsed_time(b) for a, b in evs)
+    kernel_ms = sum(kms) / len(kms)
+    log(f"[bench] {label}: step {ms_step:.4f} ms, attention call {kernel_ms:.4f} ms (median {kms[len(kms) // 2]:.4f})")
+    w = runners[0].w
+    out = {"ms_per_step": ms_step, "kernel_ms": kernel_ms, "kernel_ms_median": kms[len(kms) // 2],
+           "splits": runners[0].splits, "w": w}
+    del runners
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(budget_s=15.0):
+    """The CPU oracle, as is, on a bounded sample of the sliding-window decode workload: whole
+    sequences (all 32 q heads) until the time budget is spent.  Rate = the same algorithmic bytes
+    per second as the GPU value."""
+    import numpy as np
+    import threadpoolctl
+    import workloads as wl
+    from oracle.attention import default_scale, paged_attention, query_values
+    import torch
+    full = wl.swa_decode(device="cuda", seed=0)
+    cores = 0
+    for info in threadpoolctl.threadpool_info():
+        cores = max(cores, int(info.get("num_threads", 0)))
+    cores = cores or len(os.sched_getaffinity(0))
+    qv, _ = query_values(full.q.cpu(), "e4m3", full.q_descale.cpu())
+    bt = full.block_table.cpu().numpy()
+    cu = full.cu_seqlens_q.cpu().numpy()
+    sk = full.seqlens_k.cpu().numpy()
+    done_bytes, nseq, t_used = 0, 0, 0.0
+    for b in range(full.batch):
+        L = int(sk[b])
+        lo = max(0, L - 1 - full.window + 1)
+        pages = sorted(set(int(bt[b, n]) for n in range(lo // 64, (L - 1) // 64 + 1)))
+        ids = torch.tensor(pages, dtype=torch.long, device="cuda")
+        k = np.zeros(tuple(full.k_pool.shape), np.uint8)
+        v = np.zeros(tuple(full.v_pool.shape), np.uint8)
+        k[pages] = full.k_pool.index_select(0, ids).cpu().numpy()
+        v[pages] = full.v_pool.index_select(0, ids).cpu().numpy()
+        t0 = time.perf_counter()
+        paged_attention(qv[cu[b]:cu[b + 1]], k, v, bt[b:b + 1], np.array([0, 1]), sk[b:b + 1], full.num_kv_heads,
+                        default_scale(256), full.window, full.k_descale.cpu(), full.v_descale.cpu())
+        t_used += time.perf_counter() - t0
+        kv = (L - lo) * full.num_kv_heads * 256 * 2
+        done_bytes += kv + 32 * 256 * 1 + 32 * 256 * 2
+        nseq += 1
+        if t_used >= budget_s:
+            break
+    del full
+    torch.cuda.empty_cache()
+    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nseq} of 32 sequences of the sliding-window decode workload (all 32 q heads, "
+                      f"1024 visible keys each), numpy fp64, {t_used:.1f} s"}
+
+
+def load_traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel source; else None."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    try:
+        d = json.load(open(COUNTERS_FILE))
+    except Exception:
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    ent = d.get("kernels", {}).get(kernel_key)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true", help="only the main workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="short run for rocprofv3 counter passes: main workload plus a 1 GiB device copy")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as wl
+    import fp8_kv_cache_e4m3_amd  # noqa: F401  (fails loudly if the HIP library is missing)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    nsets = 4
+
+    if args.profile_pass:
+        # a plain copy of known size calibrates the FETCH_SIZE / WRITE_SIZE counters
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        time_workload(lambda s: wl.swa_decode(device="cuda", seed=100 + s), "decode", nsets, args.steps,
+                      args.warmup, "sliding-window decode (profile pass)")
+        return
+
+    main = time_workload(lambda s: wl.swa_decode(device="cuda", seed=100 + s), "decode", nsets, args.steps,
+                         args.warmup, "sliding-window decode")
+    w = main["w"]
+    total_b, kv_b = algo_bytes(w)
+    value = total_b / (main["ms_per_step"] * 1e-3) / 1e9
+    achieved = total_b / (main["kernel_ms"] * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic("decode_swa"),
+            "kernel": "decode_kernel<true,256> (sliding-window decode, one split)",
+            "algorithmic_bytes_per_launch": total_b}
+
+    extra = {}
+    if not args.no_extra:
+        specs = [
+            ("full_decode", lambda s: wl.full_decode(device="cuda", seed=200 + s), "decode", 4, "hbm"),
+            ("spec_verify", lambda s: wl.spec_verify(device="cuda", seed=300 + s), "decode", 2, "hbm"),
+            ("swa_prefill", lambda s: wl.swa_prefill(device="cuda", seed=400 + s), "prefill", 2, "mfma"),
+        ]
+        for name, make, entry, ns, bound in specs:
+            r = time_workload(make, entry, ns, max(5, args.steps // 5), 2, name)
+            ww = r["w"]
+            tb, kvb = algo_bytes(ww)
+            fl = algo_flops(ww)
+            e = {"workload": ww.name, "ms_per_step": round(r["ms_per_step"], 4),
+                 "attention_ms": round(r["kernel_ms"], 4), "splits": r["splits"],
+                 "kv_read_GBps": round(tb / (r["kernel_ms"] * 1e-3) / 1e9, 1),
+                 "TFLOPs": round(fl / (r["kernel_ms"] * 1e-3) / 1e12, 2)}
+            if bound == "hbm":
+                e["hbm_frac"] = round(e["kv_read_GBps"] / HBM_PEAK_GBS, 4)
+            else:
+                peak = FP8_PEAK_TFLOPS if ww.q_dtype == "e4m3" else BF16_PEAK_TFLOPS
+                e["mfma_frac"] = round(e["TFLOPs"] / peak, 4)
+            extra[name] = e
+
+    cpu = None
+    if not args.no_cpu:
+        try:
+            cpu = cpu_baseline()
+        except Exception as ex:  # the baseline must not hide the GPU result
+            log(f"[bench] cpu baseline failed: {ex!r}")
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(main["ms_per_step"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "window": w.window, "kv_len": "uniform[1024,8192]", "page": 64,
+                   "input_sets": nsets, "splits": main["splits"], "step": "quantize_q + decode_paged"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

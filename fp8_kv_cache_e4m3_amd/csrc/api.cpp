@@ -297,15 +297,20 @@ fp8attn_status fp8attn_prefill_varlen(const fp8attn_attn_args* args, hipStream_t
   if (st != FP8ATTN_OK) return st;
   if (args->total_q == 0 || args->batch == 0) return ok();
   fp8attn::AttnParams p = make_params(args);
-  const int G = args->num_q_heads / args->num_kv_heads;
-  p.row_groups = (args->max_seqlen_q * G + 15) / 16;
-  int64_t vis = args->max_seqlen_k;
-  p.num_splits = 1;
-  p.units_per_split = (int32_t)((vis + 15) / 16 + 1);
-  const int64_t grid = (int64_t)args->num_kv_heads * args->batch * p.row_groups;
-  if (grid >= (int64_t)1 << 31)
-    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: grid of %lld blocks is too large", fn, (long long)grid);
-  hipError_t e = fp8attn::launch_decode(p, args->q_dtype == FP8ATTN_E4M3, args->head_dim, grid, stream);
+  hipError_t e;
+  if (args->q_dtype == FP8ATTN_E4M3) {
+    e = fp8attn::launch_prefill_fp8(p, args->head_dim, stream);
+  } else {
+    // BF16 queries: the split-KV kernel over 16-row query tiles, one split per tile.
+    const int G = args->num_q_heads / args->num_kv_heads;
+    p.row_groups = (args->max_seqlen_q * G + 15) / 16;
+    p.num_splits = 1;
+    p.units_per_split = (int32_t)(((int64_t)args->max_seqlen_k + 15) / 16 + 1);
+    const int64_t grid = (int64_t)args->num_kv_heads * args->batch * p.row_groups;
+    if (grid >= (int64_t)1 << 31)
+      return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: grid of %lld blocks is too large", fn, (long long)grid);
+    e = fp8attn::launch_decode(p, false, args->head_dim, grid, stream);
+  }
   if (e != hipSuccess) return hip_fail(fn, e);
   return ok();
 }

@@ -48,6 +48,9 @@ hipError_t launch_quantize_q(const void* q, int64_t ntok, int32_t nheads, int32_
 hipError_t launch_decode(const AttnParams& p, bool q_e4m3, int head_dim, int64_t grid,
                          hipStream_t stream);
 
+// Native-FP8 prefill: 256 query rows per block, 64-key tiles through LDS.  head_dim 64 or 256.
+hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, hipStream_t stream);
+
 hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t S, int64_t total_q,
                           int32_t hq, int32_t d, void* out, int64_t out_stride_tok,
                           int64_t out_stride_head, float* lse_out, hipStream_t stream);

@@ -267,6 +267,10 @@ def test_per_sequence_head_descales():
 
 def test_null_descales_and_no_lse():
     w = wl.custom("bf16", 512, 8, 2, -1, [333], [1], seed=23)
+    # unit descales: the codes themselves are N(0,1) values
+    g = torch.Generator().manual_seed(23)
+    w.k_pool = torch.randn(w.k_pool.shape, generator=g).to(torch.float8_e4m3fn).view(torch.uint8)
+    w.v_pool = torch.randn(w.v_pool.shape, generator=g).to(torch.float8_e4m3fn).view(torch.uint8)
     w.k_descale = torch.tensor([1.0])
     w.v_descale = torch.tensor([1.0])
     o_ref, l_ref, _ = oracle_run(w)

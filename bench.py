@@ -241,8 +241,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="only the main workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--profile-pass", action="store_true",
-                    help="short run for rocprofv3 counter passes: main workload plus a 1 GiB device copy")
+    ap.add_argument("--profile-pass", default=None,
+                    choices=["swa_decode", "full_decode", "spec_verify", "swa_prefill"],
+                    help="short run for rocprofv3 counter passes: one workload plus a 1 GiB device copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -256,16 +257,23 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     nsets = 4
 
+    makers = {
+        "swa_decode": (lambda s: wl.swa_decode(device="cuda", seed=100 + s), "decode"),
+        "full_decode": (lambda s: wl.full_decode(device="cuda", seed=200 + s), "decode"),
+        "spec_verify": (lambda s: wl.spec_verify(device="cuda", seed=300 + s), "decode"),
+        "swa_prefill": (lambda s: wl.swa_prefill(device="cuda", seed=400 + s), "prefill"),
+    }
     if args.profile_pass:
-        # a plain copy of known size calibrates the FETCH_SIZE / WRITE_SIZE counters
+        # a plain copy of known size (1 GiB read + 1 GiB written) calibrates FETCH_SIZE / WRITE_SIZE
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-        time_workload(lambda s: wl.swa_decode(device="cuda", seed=100 + s), "decode", nsets, args.steps,
-                      args.warmup, "sliding-window decode (profile pass)")
+        torch.cuda.empty_cache()
+        make, entry = makers[args.profile_pass]
+        time_workload(make, entry, 2, args.steps, args.warmup, f"{args.profile_pass} (profile pass)")
         return
 
     main = time_workload(lambda s: wl.swa_decode(device="cuda", seed=100 + s), "decode", nsets, args.steps,

@@ -18,7 +18,7 @@ import torch  # must be imported before the library: the library reuses torch's 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8attn.so")
 
 if not os.path.exists(_LIB_PATH):
-    raise ImportError(f"{_LIB_PATH} is not built; run `python -m fp8_kv_cache_e4m3_amd.build` "
+    raise ImportError(f"{_LIB_PATH} is not built; run `python fp8_kv_cache_e4m3_amd/build.py` "
                       "(there is no non-HIP fallback)")
 _lib = ctypes.CDLL(_LIB_PATH)
 

@@ -1,6 +1,6 @@
 """Build libfp8attn.so in-tree with hipcc for gfx950.
 
-    python -m fp8_kv_cache_e4m3_amd.build        # or fp8_kv_cache_e4m3_amd.build.build()
+    python fp8_kv_cache_e4m3_amd/build.py        # runs without importing (and loading) the package
 
 Every source is compiled on each call (no stale objects); objects go to ``_build/``
 next to this file and the shared library lands in this package directory.
@@ -74,6 +74,11 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # A kernel whose host stub is missing links fine but fails at load time: catch it here.
+    r = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        raise RuntimeError("kernel host stubs are undefined in the linked library: " + ", ".join(missing))
     shutil.move(tmp, LIB)
     if verbose:
         print(f"[build] {LIB}")

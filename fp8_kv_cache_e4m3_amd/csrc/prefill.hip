@@ -64,6 +64,9 @@ __device__ __forceinline__ void unpack4_e4m3(uint32_t w, float out[4]) {
   out[3] = hi[1];
 }
 
+// MFMA row m of a 32-key half tile holds key kperm(m): bits 2 and 3 of m swapped.
+__device__ __forceinline__ int kperm(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
 template <int D>
 struct PrefillShape {
   static constexpr int NW = 8;            // waves per block
@@ -77,8 +80,28 @@ struct PrefillShape {
   static constexpr int SLOTS = NCH + 1;   // 16-byte LDS slots per key row
   static constexpr int TILE = BK * RS;    // bytes of one K (or V) tile in LDS
   static constexpr int LOADS = 2 * SLOTS; // wave-wide 1 KiB load instructions per K+V tile
+  static constexpr int MAXI = (LOADS + NW - 1) / NW;  // load instructions per wave per tile
   static_assert(D == 64 || D == 256, "head dim");
 };
+
+// Issue this wave's direct-to-LDS loads of one K and one V tile (instructions wave, wave + 8,
+// ...).  lds_stage points at [K tile | V tile] of one stage.
+template <int D>
+__device__ __forceinline__ void load_tile_to_lds(const uint8_t* ktb, const uint8_t* vtb, const uint32_t* loff,
+                                                 int wave, uint8_t* lds_stage) {
+  using S = PrefillShape<D>;
+#pragma unroll
+  for (int t = 0; t < S::MAXI; ++t) {
+    const int ins = wave + S::NW * t;
+    if (ins < S::LOADS) {
+      const int which = ins / S::SLOTS;
+      const int blk = ins % S::SLOTS;
+      __builtin_amdgcn_global_load_lds((which ? vtb : ktb) + loff[t],
+                                       (__attribute__((address_space(3))) void*)(lds_stage + which * S::TILE + blk * 1024),
+                                       16, 0, 0);
+    }
+  }
+}
 
 template <int D, bool SPLIT>
 __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, int32_t nqb) {
@@ -163,25 +186,30 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   // ---- tile loader: HBM -> LDS directly (global_load_lds_dwordx4, 16 bytes per lane) ---------
   // A wave-wide instruction fills 64 consecutive 16-byte LDS slots (lane i -> slot i).  Key rows
   // occupy D/16 + 1 slots: D bytes of data and one pad slot, which receives a duplicate of the
-  // row's first chunk.  The pad makes the row stride D + 16 bytes, so rows that the operand
-  // reads touch together land in different banks while every read address stays a per-lane base
-  // plus a compile-time offset.
+  // row's first chunk.  The pad makes the row stride D + 16 bytes (see the operand reads).
+  // Wave w issues instructions w, w + 8, ...; each lane's byte offset inside the 64-key tile is
+  // fixed, so it is computed once and every load is a scalar tile base plus that offset.
+  uint32_t loff[S::MAXI];
+#pragma unroll
+  for (int t = 0; t < S::MAXI; ++t) {
+    const int ins = wave + S::NW * t;
+    const int sl = (ins % S::SLOTS) * 64 + lane;
+    const int row = sl / S::SLOTS, posn = sl % S::SLOTS;
+    loff[t] = (uint32_t)(row * sT) + 16u * (uint32_t)(posn == S::NCH ? 0 : posn);
+  }
   auto issue = [&](int kt, int stage) {
     const int j0 = kt * S::BK;
-    const int64_t page = bt[j0 / ps];
-    const int slot0 = j0 % ps;
-    for (int ins = wave; ins < S::LOADS; ins += S::NW) {
-      const int which = ins / S::SLOTS;
-      const int blk = ins % S::SLOTS;
-      const int sl = blk * 64 + lane;
-      const int row = sl / S::SLOTS, posn = sl % S::SLOTS;
-      const int chunk = posn == S::NCH ? 0 : posn;
-      const uint8_t* src = (which ? vbase : kbase) + page * sP + (int64_t)(slot0 + row) * sT + 16 * chunk;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&lds[stage][which][blk * 1024],
-                                       16, 0, 0);
-    }
+    int pidx, slot0;
+    if (ps == S::BK) { pidx = kt; slot0 = 0; } else { pidx = j0 / ps; slot0 = j0 - pidx * ps; }
+    const int64_t tile_off = (int64_t)bt[pidx] * sP + (int64_t)slot0 * sT;
+    load_tile_to_lds<D>(kbase + tile_off, vbase + tile_off, loff, wave, &lds[stage][0][0]);
   };
 
+  // Row assignments.  MFMA row m of a 32-key half tile holds key kperm(m), which swaps bits 2
+  // and 3 of m.  Then the 8 keys one transposing read gathers are 8 consecutive keys, and the
+  // two 16-lane halves of the read (d rows 0..15 and 16..31 of an O^T tile, which hold d and
+  // d + D/2) touch 16 distinct 16-byte LDS slots: no bank conflicts with the D + 16 row stride.
+  // O^T tile dt, row m holds d = 16*dt + m for m < 16 and d = 16*dt + D/2 + (m - 16) otherwise.
   // per-lane constants for the V^T transposing reads
   const int tr_blk = (lane >> 4) & 1;        // which 16-row half of the 32 d-rows
   const int tr_j = (lane & 15) >> 1;         // source row j (0..7) supplied by this lane
@@ -196,7 +224,7 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       sacc[st] = f32x16_t{};
-      const int krow = 32 * st + lr;              // A operand row = key
+      const int krow = 32 * st + kperm(lr);       // A operand row m holds key kperm(m)
       const uint8_t* rowp = ktile + krow * S::RS + 32 * lg;
 #pragma unroll
       for (int c = 0; c < S::KSTEP; ++c) {
@@ -206,24 +234,26 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
         sacc[st] = mfma_fp8_32x32x64(ka, qop[c], sacc[st], kE8M0One);
       }
     }
-    // scale, mask (boundary tiles only), tile max
+    // mask (boundary tiles only) and tile max, on unscaled scores (the scale is positive)
     const bool need_mask = !(j0 >= wfull_lo && j0 + S::BK - 1 <= wpf);
-    float mx = kNegInf;
+    float mxr = kNegInf;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float v = sacc[st][i] * cs;
+        float v = sacc[st][i];
         if (need_mask) {
-          const int j = j0 + 32 * st + 8 * (i >> 2) + 4 * lg + (i & 3);
+          // value i of this lane is S^T row 8*(i/4) + 4*lg + i%4, i.e. key kperm(that row)
+          const int j = j0 + 32 * st + ((i >> 3) << 4) + (lg << 3) + (((i >> 2) & 1) << 2) + (i & 3);
           const bool vis = j <= pos && (W < 1 || j > pos - W);
           v = vis ? v : kNegInf;
+          sacc[st][i] = v;
         }
-        sacc[st][i] = v;
-        mx = fmaxf(mx, v);
+        mxr = fmaxf(mxr, v);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mxr = fmaxf(mxr, __shfl_xor(mxr, 32, 64));
+    const float mx = mxr * cs;
     // lazy maximum: move it only when the tile exceeds it by more than 2^8
     const bool grow = mx > m_used + kLazyMax;
     if (__any(grow)) {
@@ -237,8 +267,8 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
 #pragma unroll
       for (int t = 0; t < S::NDT; ++t) oacc[t] *= a;
     }
-    const float m_use = m_used == kNegInf ? 0.f : m_used;
-    // P = exp2(s - m), packed to E4M3 in the B-operand slot order (slot 16*st + i)
+    const float neg_m = m_used == kNegInf ? 0.f : -m_used;
+    // P = exp2(s * cs - m), packed to E4M3 in the B-operand slot order (slot 16*st + i)
     i32x8_t pb, pl = {};
     float lsum = 0.f;
 #pragma unroll
@@ -248,7 +278,7 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
         float e[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          e[k] = fast_exp2(sacc[st][4 * q4 + k] - m_use);
+          e[k] = fast_exp2(__builtin_fmaf(sacc[st][4 * q4 + k], cs, neg_m));
           lsum += e[k];
         }
         const uint32_t hi = pack4_e4m3(e[0], e[1], e[2], e[3]);
@@ -266,11 +296,12 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
     // O^T += V^T * P^T : for each 32-row d tile, gather 32 keys per lane with 4 transposing reads
 #pragma unroll
     for (int dt = 0; dt < S::NDT; ++dt) {
-      const int col = 32 * dt + 16 * tr_blk + 8 * tr_h;
+      const int col = 16 * dt + (D / 2) * tr_blk + 8 * tr_h;
       i32x8_t va;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int key = 32 * (q >> 1) + 16 * (q & 1) + 8 * (tr_j >> 2) + 4 * lg + (tr_j & 3);
+        // slots 8q..8q+7 of group lg hold the 8 consecutive keys 32(q/2) + 16(q%2) + 8*lg + j
+        const int key = 32 * (q >> 1) + 16 * (q & 1) + 8 * lg + tr_j;
         const uint8_t* src = vtile + key * S::RS + col;
         const i32x2_t v2 = lds_read_tr8(src);
         va[2 * q] = v2[0];
@@ -305,7 +336,7 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   for (int dt = 0; dt < S::NDT; ++dt) {
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const int d = 32 * dt + 8 * i4 + 4 * lg;
+      const int d = 16 * dt + (i4 >= 2 ? D / 2 : 0) + 8 * (i4 & 1) + 4 * lg;
       const bf16x4_t o = {(__bf16)(oacc[dt][4 * i4] * inv), (__bf16)(oacc[dt][4 * i4 + 1] * inv),
                           (__bf16)(oacc[dt][4 * i4 + 2] * inv), (__bf16)(oacc[dt][4 * i4 + 3] * inv)};
       *reinterpret_cast<bf16x4_t*>(op + d) = o;

@@ -41,7 +41,8 @@ def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC] + COMMON + lang + ["-c", path, "-o", obj]
+    extra = os.environ.get("EXTRA_HIPCC_FLAGS", "").split()   # e.g. -D tuning switches for experiments
+    cmd = [HIPCC] + COMMON + extra + lang + ["-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -45,31 +45,48 @@ struct UnitRegs {
   uint32_t v[4][DecodeShape<D>::VBLK][DecodeShape<D>::CW / 4];
 };
 
-template <int D>
+// K/V byte loads; NT marks them non-temporal (streamed once, no reuse).
+template <bool NT, class T>
+__device__ __forceinline__ T stream_load(const T* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <int D, bool NT>
 __device__ __forceinline__ void load_unit(UnitRegs<D>& ur, const uint8_t* __restrict__ kpage,
                                           const uint8_t* __restrict__ vpage, int64_t sT, int slot0,
                                           int col, int grp) {
   using S = DecodeShape<D>;
   const uint8_t* kp = kpage + (int64_t)(slot0 + col) * sT + 16 * grp;
 #pragma unroll
-  for (int c = 0; c < S::KCH; ++c) ur.k[c] = *reinterpret_cast<const u32x4_t*>(kp + 64 * c);
+  for (int c = 0; c < S::KCH; ++c) ur.k[c] = stream_load<NT>(reinterpret_cast<const u32x4_t*>(kp + 64 * c));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint8_t* vp = vpage + (int64_t)(slot0 + 4 * grp + i) * sT + col * S::CW;
 #pragma unroll
     for (int blk = 0; blk < S::VBLK; ++blk) {
       if constexpr (S::CW == 16) {
-        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(vp + blk * 16 * S::CW);
+        const u32x4_t w = stream_load<NT>(reinterpret_cast<const u32x4_t*>(vp + blk * 16 * S::CW));
         ur.v[i][blk][0] = w[0];
         ur.v[i][blk][1] = w[1];
         ur.v[i][blk][2] = w[2];
         ur.v[i][blk][3] = w[3];
       } else {
-        ur.v[i][blk][0] = *reinterpret_cast<const uint32_t*>(vp + blk * 16 * S::CW);
+        ur.v[i][blk][0] = stream_load<NT>(reinterpret_cast<const uint32_t*>(vp + blk * 16 * S::CW));
       }
     }
   }
 }
+
+// Per-variant tuning (measured on MI355X): register ring depth and non-temporal K/V loads.
+// Deeper rings need more than 256 registers at d256 (one wave per SIMD instead of two), which
+// measured slower; at d512 a third buffer spills.  Non-temporal loads help the d256 stream
+// (+5%) and hurt the split d512 stream (-11%).
+template <bool QFP8, int D>
+struct DecodeTune {
+  static constexpr int NBUF = 2;
+  static constexpr bool NT = QFP8 && D == 256;
+};
 
 template <bool QFP8, int D>
 struct QRegs;
@@ -81,6 +98,12 @@ struct QRegs<false, D> { bf16x8_t q[2 * DecodeShape<D>::KCH]; };
 template <bool QFP8, int D>
 __global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
   using S = DecodeShape<D>;
+  using T = DecodeTune<QFP8, D>;
+  constexpr int NBUF = T::NBUF;
+  // LDS: the 4 waves' softmax state and O tiles for the final merge
+  __shared__ __attribute__((aligned(16))) float sm_o[4][16][S::RS];
+  __shared__ float sm_m[4][16];
+  __shared__ float sm_l[4][16];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
@@ -131,28 +154,25 @@ __global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
 
   // ---- Q^T operand (rows on lane columns) ---------------------------------------------------
   QRegs<QFP8, D> qr;
-  {
-    if constexpr (QFP8) {
-      const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)(t0 + tok) * p.q_stride_tok +
-                          (int64_t)hq * p.q_stride_head + 16 * grp;
+  if constexpr (QFP8) {
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)(t0 + tok) * p.q_stride_tok +
+                        (int64_t)hq * p.q_stride_head + 16 * grp;
 #pragma unroll
-      for (int c = 0; c < S::KCH; ++c) {
-        u32x4_t w = rvalid ? *reinterpret_cast<const u32x4_t*>(qp + 64 * c) : u32x4_t{0, 0, 0, 0};
-        qr.q[2 * c] = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
-        qr.q[2 * c + 1] = (uint64_t)w[2] | ((uint64_t)w[3] << 32);
-      }
-    } else {
-      const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)(t0 + tok) * p.q_stride_tok +
-                         (int64_t)hq * p.q_stride_head + 16 * grp;
+    for (int c = 0; c < S::KCH; ++c) {
+      u32x4_t w = rvalid ? *reinterpret_cast<const u32x4_t*>(qp + 64 * c) : u32x4_t{0, 0, 0, 0};
+      qr.q[2 * c] = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
+      qr.q[2 * c + 1] = (uint64_t)w[2] | ((uint64_t)w[3] << 32);
+    }
+  } else {
+    const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)(t0 + tok) * p.q_stride_tok +
+                       (int64_t)hq * p.q_stride_head + 16 * grp;
 #pragma unroll
-      for (int c = 0; c < S::KCH; ++c) {
-        const bf16x8_t z = {};
-        qr.q[2 * c] = rvalid ? *reinterpret_cast<const bf16x8_t*>(qp + 64 * c) : z;
-        qr.q[2 * c + 1] = rvalid ? *reinterpret_cast<const bf16x8_t*>(qp + 64 * c + 8) : z;
-      }
+    for (int c = 0; c < S::KCH; ++c) {
+      const bf16x8_t z = {};
+      qr.q[2 * c] = rvalid ? *reinterpret_cast<const bf16x8_t*>(qp + 64 * c) : z;
+      qr.q[2 * c + 1] = rvalid ? *reinterpret_cast<const bf16x8_t*>(qp + 64 * c + 8) : z;
     }
   }
-
   f32x4_t oacc[S::NT];
 #pragma unroll
   for (int t = 0; t < S::NT; ++t) oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -168,7 +188,7 @@ __global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
     const int j0 = u * 16;
     const int64_t page = bt[j0 / ps];
     const int slot0 = j0 % ps;
-    load_unit<D>(ur, kbase + page * sP, vbase + page * sP, sT, slot0, col, grp);
+    load_unit<D, T::NT>(ur, kbase + page * sP, vbase + page * sP, sT, slot0, col, grp);
   };
 
   auto compute = [&](const UnitRegs<D>& ur, int u) {
@@ -231,26 +251,28 @@ __global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
   };
 
   // ---- main loop: this wave takes units su0+wave, su0+wave+4, ... --------------------------
+  // A ring of NBUF register buffers: NBUF - 1 units stay in flight while one is computed.  Every
+  // trip issues the same loads (indices past the end are clamped to the split's last unit, an
+  // in-bounds re-read that hits L2), so the compiler can wait for exactly the oldest unit
+  // instead of draining every outstanding load.
   {
-    UnitRegs<D> bufA, bufB;
-    int u = su0 + wave;
-    if (u < su1) issue(bufA, u);
-    if (u + 4 < su1) issue(bufB, u + 4);
-    for (; u < su1; u += 8) {
-      compute(bufA, u);
-      if (u + 8 < su1) issue(bufA, u + 8);
-      if (u + 4 < su1) {
-        compute(bufB, u + 4);
-        if (u + 12 < su1) issue(bufB, u + 12);
+    UnitRegs<D> buf[NBUF];
+    const int u0 = su0 + wave;
+    const int ulast = su1 - 1;
+#pragma unroll
+    for (int k = 0; k < NBUF; ++k) issue(buf[k], min(u0 + 4 * k, ulast));
+    for (int u = u0; u < su1; u += 4 * NBUF) {
+#pragma unroll
+      for (int k = 0; k < NBUF; ++k) {
+        const int uk = u + 4 * k;
+        if (uk < su1) compute(buf[k], uk);
+        issue(buf[k], min(uk + 4 * NBUF, ulast));
       }
     }
   }
   l_run = sum_over_groups(l_run);
 
   // ---- merge the 4 waves through LDS --------------------------------------------------------
-  __shared__ float sm_m[4][16];
-  __shared__ float sm_l[4][16];
-  __shared__ float sm_o[4][16][S::RS];
   if (grp == 0) {
     sm_m[wave][col] = m_run;
     sm_l[wave][col] = l_run;

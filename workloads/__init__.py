@@ -114,13 +114,18 @@ def _amax_descale(x: torch.Tensor) -> torch.Tensor:
     return (amax / torch.tensor(E4M3_MAX, dtype=torch.float32, device=x.device)).reshape(1)
 
 
-def _e4m3_pool(rng: _Rng, num_pages: int, num_kv_heads: int, d: int, chunk_pages: int = 2048):
+def _e4m3_pool(rng: _Rng, num_pages: int, num_kv_heads: int, d: int, chunk_pages: int = 2048,
+               layout: str = "token_major"):
     """Draw a pool [pages, 64, Hkv, d] from N(0,1) and store it as E4M3 bytes.
 
     The descale is amax over the whole pool / 448.  Large pools are drawn in
     chunks so that the fp32 staging stays bounded: the chunk draws happen in a
     fixed order, so the result depends only on the seed."""
     dev = rng.device
+    if layout == "head_major":
+        # physical order [pages, Hkv, 64, d] (one contiguous tile per page and kv head), returned as a
+        # [pages, 64, Hkv, d] view: the logical indexing is the same, only the strides differ
+        return _e4m3_pool_hm(rng, num_pages, num_kv_heads, d, chunk_pages)
     shape_tail = (PAGE, num_kv_heads, d)
     if num_pages * PAGE * num_kv_heads * d <= (1 << 27):
         x = rng.normal((num_pages,) + shape_tail)
@@ -129,7 +134,6 @@ def _e4m3_pool(rng: _Rng, num_pages: int, num_kv_heads: int, d: int, chunk_pages
         return codes.contiguous(), ds
     # two passes: first draw chunks and record amax, then redraw with the same seed state copy
     state_np = None
-    chunks = []
     amax = torch.zeros((), dtype=torch.float32, device=dev)
     gen_state = rng.gen.get_state() if rng.gen is not None else None
     if rng.gen is None:
@@ -153,8 +157,15 @@ def _e4m3_pool(rng: _Rng, num_pages: int, num_kv_heads: int, d: int, chunk_pages
     return out, ds
 
 
+def _e4m3_pool_hm(rng: _Rng, num_pages: int, num_kv_heads: int, d: int, chunk_pages: int):
+    """Head-major pool: drawn in physical order [pages, Hkv, 64, d], viewed as [pages, 64, Hkv, d]."""
+    phys, ds = _e4m3_pool(rng, num_pages, 1, num_kv_heads * d, chunk_pages)   # [pages, 64, 1, Hkv*d] bytes
+    phys = phys.reshape(num_pages, num_kv_heads, PAGE, d)                     # reinterpret the same bytes
+    return phys.permute(0, 2, 1, 3), ds
+
+
 def _assemble(name, rng: _Rng, q_dtype, d, hq, hkv, window, seqlens, qlens,
-              shared_prefix_pages: int = 0, fixed_table=None) -> Workload:
+              shared_prefix_pages: int = 0, fixed_table=None, layout: str = "token_major") -> Workload:
     dev = rng.device
     B = len(seqlens)
     npages = [math.ceil(L / PAGE) for L in seqlens]
@@ -177,8 +188,8 @@ def _assemble(name, rng: _Rng, q_dtype, d, hq, hkv, window, seqlens, qlens,
     q_descale = None
     if q_dtype == "e4m3":
         q_descale = _amax_descale(q.to(torch.float32))
-    k_pool, k_ds = _e4m3_pool(rng, pool_pages, hkv, d)
-    v_pool, v_ds = _e4m3_pool(rng, pool_pages, hkv, d)
+    k_pool, k_ds = _e4m3_pool(rng, pool_pages, hkv, d, layout=layout)
+    v_pool, v_ds = _e4m3_pool(rng, pool_pages, hkv, d, layout=layout)
     cu = np.zeros(B + 1, dtype=np.int64)
     cu[1:] = np.cumsum(qlens)
     i32 = lambda a: torch.as_tensor(np.asarray(a, dtype=np.int32)).to(dev)
@@ -199,7 +210,7 @@ def tiny(q_dtype: str = "bf16", device="cpu", seed: int = 0) -> Workload:
                      fixed_table=[[1, 0]])
 
 
-def swa_decode(device="cpu", seed: int = 2, scale: float = 1.0) -> Workload:
+def swa_decode(device="cpu", layout: str = "token_major", seed: int = 2, scale: float = 1.0) -> Workload:
     """Sliding-window decode: batch 32, one query token each, KV lengths uniform in
     [1024, 8192], 32 q / 16 kv heads, d 256, window 1024, E4M3 Q/K/V."""
     rng = _Rng(seed, device)
@@ -208,10 +219,10 @@ def swa_decode(device="cpu", seed: int = 2, scale: float = 1.0) -> Workload:
     W = max(1, int(1024 * scale))
     seqlens = rng.lengths(lo, hi, B)
     return _assemble(f"sliding-window decode B{B} d256 W{W}", rng, "e4m3", 256, 32, 16, W,
-                     seqlens, [1] * B)
+                     seqlens, [1] * B, layout=layout)
 
 
-def full_decode(device="cpu", seed: int = 3, scale: float = 1.0) -> Workload:
+def full_decode(device="cpu", layout: str = "token_major", seed: int = 3, scale: float = 1.0) -> Workload:
     """Full-attention decode: batch 64, one query token each, KV lengths uniform in
     [8192, 32768], 32 q / 4 kv heads (GQA 8), d 512, bf16 Q with E4M3 K/V, causal."""
     rng = _Rng(seed, device)
@@ -219,10 +230,10 @@ def full_decode(device="cpu", seed: int = 3, scale: float = 1.0) -> Workload:
     lo, hi = max(1, int(8192 * scale)), max(2, int(32768 * scale))
     seqlens = rng.lengths(lo, hi, B)
     return _assemble(f"full-attention decode B{B} d512", rng, "bf16", 512, 32, 4, -1,
-                     seqlens, [1] * B)
+                     seqlens, [1] * B, layout=layout)
 
 
-def swa_prefill(device="cpu", seed: int = 4, scale: float = 1.0) -> Workload:
+def swa_prefill(device="cpu", layout: str = "token_major", seed: int = 4, scale: float = 1.0) -> Workload:
     """Chunked prefill, sliding-window layer: 8 sequences of 8192 new tokens each (no prior
     cache), 32 q / 16 kv heads, d 256, causal + window 1024, E4M3 Q/K/V."""
     rng = _Rng(seed, device)
@@ -230,10 +241,10 @@ def swa_prefill(device="cpu", seed: int = 4, scale: float = 1.0) -> Workload:
     L = max(1, int(8192 * scale))
     W = max(1, int(1024 * scale))
     return _assemble(f"sliding-window prefill B{B}x{L} d256 W{W}", rng, "e4m3", 256, 32, 16, W,
-                     [L] * B, [L] * B)
+                     [L] * B, [L] * B, layout=layout)
 
 
-def spec_verify(device="cpu", seed: int = 5, scale: float = 1.0) -> Workload:
+def spec_verify(device="cpu", layout: str = "token_major", seed: int = 5, scale: float = 1.0) -> Workload:
     """Spec-decode verify with a shared prefix: 64 sequences, each a 25,600-token prefix whose
     pages every sequence shares, plus 3,072 unique tokens; 4 query tokens (1 + 3 speculative)
     at the end, causal among themselves; 32 q / 4 kv heads, d 512, bf16 Q, E4M3 K/V."""
@@ -243,15 +254,15 @@ def spec_verify(device="cpu", seed: int = 5, scale: float = 1.0) -> Workload:
     unique_pages = max(1, int(round(48 * scale)))
     L = (prefix_pages + unique_pages) * PAGE
     return _assemble(f"spec-verify shared prefix B{B} L{L} d512", rng, "bf16", 512, 32, 4, -1,
-                     [L] * B, [4] * B, shared_prefix_pages=prefix_pages)
+                     [L] * B, [4] * B, shared_prefix_pages=prefix_pages, layout=layout)
 
 
 def custom(q_dtype: str, d: int, hq: int, hkv: int, window: int, seqlens, qlens,
-           device="cpu", seed: int = 7, shared_prefix_pages: int = 0) -> Workload:
+           device="cpu", seed: int = 7, shared_prefix_pages: int = 0, layout: str = "token_major") -> Workload:
     """Any shape, same recipe (used by edge-case tests)."""
     rng = _Rng(seed, device)
     return _assemble(f"custom d{d} {hq}/{hkv} W{window}", rng, q_dtype, d, hq, hkv, window,
-                     list(seqlens), list(qlens), shared_prefix_pages=shared_prefix_pages)
+                     list(seqlens), list(qlens), shared_prefix_pages=shared_prefix_pages, layout=layout)
 
 
 BY_NAME = {

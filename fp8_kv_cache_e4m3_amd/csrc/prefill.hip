@@ -10,8 +10,11 @@
 //    group) pairs, token-major, so one K/V tile serves every q head of the group.  Each wave
 //    owns 32 rows.
 //  * K and V arrive one 64-token page at a time straight from HBM into LDS
-//    (global_load_lds_dwordx4), double buffered, with one barrier per tile.  Key rows are padded
-//    to D + 16 bytes so that the MFMA operand reads below are free of bank conflicts.
+//    (global_load_lds_dwordx4) in a ring of three stages.  Key rows are padded to D + 16 bytes
+//    so that the MFMA operand reads below are free of bank conflicts.
+//  * The 8 waves form two groups half a tile apart, one barrier per tile: while one wave of a
+//    SIMD runs the softmax of a tile on the VALU, its partner runs MFMAs (PV of the previous tile
+//    and QK^T of the next), so the matrix cores and the VALU overlap.
 //  * S^T = K * Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales): keys are the MFMA rows,
 //    query rows the columns, so each query row lives on one lane column (lane % 32) and its
 //    softmax state is per lane, reduced across the two 32-lane halves with one exchange.
@@ -25,6 +28,9 @@
 //    (SPLIT = true) that also feeds the residual p - e4m3(p), scaled by 16, through a second
 //    MFMA with a 2^-4 operand scale (P = hi + lo).  Keeping it a separate instance keeps the
 //    common instance within 256 registers (2 waves per SIMD).
+#include <algorithm>
+#include <type_traits>
+
 #include "device.h"
 #include "params.h"
 
@@ -64,6 +70,15 @@ __device__ __forceinline__ void unpack4_e4m3(uint32_t w, float out[4]) {
   out[3] = hi[1];
 }
 
+// A per-lane LDS byte offset the optimiser treats as opaque, so that it is not split into a chain
+// of address computations.  Every operand read is then the stage array plus this offset plus a
+// constant, and the LDS lowering can still tell which array (stage) each read touches: that is
+// what lets a read of one stage proceed while direct-to-LDS loads into another are in flight.
+__device__ __forceinline__ int lane_offset(int x) {
+  asm("" : "+v"(x));
+  return x;
+}
+
 // MFMA row m of a 32-key half tile holds key kperm(m): bits 2 and 3 of m swapped.
 __device__ __forceinline__ int kperm(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
@@ -81,33 +96,117 @@ struct PrefillShape {
   static constexpr int TILE = BK * RS;    // bytes of one K (or V) tile in LDS
   static constexpr int LOADS = 2 * SLOTS; // wave-wide 1 KiB load instructions per K+V tile
   static constexpr int MAXI = (LOADS + NW - 1) / NW;  // load instructions per wave per tile
+  static_assert(MAXI <= NDT + 2 * KSTEP, "loads are issued one per MFMA");
   static_assert(D == 64 || D == 256, "head dim");
 };
 
-// Issue this wave's direct-to-LDS loads of one K and one V tile (instructions wave, wave + 8,
-// ...).  lds_stage points at [K tile | V tile] of one stage.
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One wave-wide direct-to-LDS load: lane i copies the 16 bytes at gbase + voff (voff per lane)
+// to LDS address lds_dst + 16 i.  It is issued from inline assembly on purpose: the compiler
+// then does not track it, and the kernel alone orders these loads against the LDS reads (every
+// wave waits for its own loads, vmcnt(0), before the barrier that publishes a tile).  When the
+// compiler tracks them itself, it cannot prove that reads of one stage are independent of loads
+// into another across loop iterations and drains all loads in flight before every read.
+// M0 holds the LDS address; gfx9 needs one wait state between an SALU write of M0 and the load
+// that reads it.  M0 is not otherwise live in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const uint8_t* gbase, uint32_t voff, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(lds_dst)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Direct-to-LDS loads of one K and one V tile: D/16 + 1 16-byte slots per key row (the pad slot
+// gets a copy of the row's first chunk), 64 lanes per instruction, 2 * (D/16 + 1) instructions
+// per tile.  Wave w issues instructions w, w + 8, ...; every wave issues MAXI of them, a wave
+// that has one fewer repeating its previous one (the same bytes to the same place), so that the
+// issue is branch-free and every wave has the same number of loads in flight.
+struct TileLoad {
+  const uint8_t* k_src;   // K tile (page base plus the tile's first slot), uniform
+  const uint8_t* v_src;   // V tile
+  uint32_t lds_stage;     // LDS address of the stage's [K tile | V tile]
+};
 template <int D>
-__device__ __forceinline__ void load_tile_to_lds(const uint8_t* ktb, const uint8_t* vtb, const uint32_t* loff,
-                                                 int wave, uint8_t* lds_stage) {
+__device__ __forceinline__ int load_instruction(int wave, int k) {
   using S = PrefillShape<D>;
+  const int ins = wave + S::NW * k;
+  return ins < S::LOADS ? ins : ins - S::NW;
+}
+template <int D>
+__device__ __forceinline__ void tile_load_step(const TileLoad& tl, const uint32_t* loff, int wave, int k) {
+  using S = PrefillShape<D>;
+  const int ins = load_instruction<D>(wave, k);
+  const int which = ins / S::SLOTS;
+  const int blk = ins % S::SLOTS;
+  lds_dma16(which ? tl.v_src : tl.k_src, loff[k], tl.lds_stage + (uint32_t)(which * S::TILE + blk * 1024));
+}
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector memory operations of
+// this wave are outstanding and leaves the other counters unconstrained
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// The MFMA work of one wave between two barriers: O^T += V^T * P^T for one tile (PV) and then
+// S^T = K * Q^T for another (QK).  Operands are read from LDS two MFMAs ahead of their use, in a
+// ring of three operand registers, so the LDS latency hides behind the MFMAs instead of
+// stalling each one; the schedule barriers keep exactly that order.
+//  * PV op dt (d tile of 32 rows): four transposing reads gather 32 keys per lane.  Slots
+//    8q..8q+7 of lane group lg hold the 8 consecutive keys 32(q/2) + 16(q%2) + 8*lg + j, where j
+//    is the source row this lane supplies; vp already holds the lane's part of the address.
+//  * QK op (h2, c): key rows 32*h2 + kperm(m) (kp holds the lane's row and half), d bytes
+//    64c .. 64c + 63.  The two 32-key halves alternate so consecutive MFMAs are independent.
+template <int D, bool SPLIT>
+__device__ __forceinline__ void mfma_stream(const uint8_t* vp, const uint8_t* kp,
+                                            f32x16_t (&oacc)[PrefillShape<D>::NDT], f32x16_t (&sacc)[2],
+                                            const i32x8_t& pb, const i32x8_t& pbl,
+                                            const i32x8_t (&qop)[PrefillShape<D>::KSTEP]) {
+  using S = PrefillShape<D>;
+  constexpr int NPV = S::NDT;
+  constexpr int NOPS = NPV + 2 * S::KSTEP;
+  i32x8_t buf[3];
 #pragma unroll
-  for (int t = 0; t < S::MAXI; ++t) {
-    const int ins = wave + S::NW * t;
-    if (ins < S::LOADS) {
-      const int which = ins / S::SLOTS;
-      const int blk = ins % S::SLOTS;
-      __builtin_amdgcn_global_load_lds((which ? vtb : ktb) + loff[t],
-                                       (__attribute__((address_space(3))) void*)(lds_stage + which * S::TILE + blk * 1024),
-                                       16, 0, 0);
+  for (int j = 0; j < NOPS + 2; ++j) {
+    if (j < NOPS) {
+      i32x8_t& o = buf[j % 3];
+      if (j < NPV) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const i32x2_t v2 = lds_read_tr8(vp + ((32 * (q >> 1) + 16 * (q & 1)) * S::RS + 16 * j));
+          o[2 * q] = v2[0];
+          o[2 * q + 1] = v2[1];
+        }
+      } else {
+        const int idx = j - NPV, h2 = idx & 1, c = idx >> 1;
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(kp + (32 * h2 * S::RS + 64 * c));
+        const u32x4_t y = *reinterpret_cast<const u32x4_t*>(kp + (32 * h2 * S::RS + 64 * c + 16));
+        o = i32x8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);   // the reads of op j go out before the MFMA of op j - 2
+    if (j >= 2) {
+      const int i = j - 2;
+      const i32x8_t& a = buf[i % 3];
+      if (i < NPV) {
+        oacc[i] = mfma_fp8_32x32x64(a, pb, oacc[i], kE8M0One);
+        if constexpr (SPLIT) oacc[i] = mfma_fp8_32x32x64(a, pbl, oacc[i], kE8M0Sixteenth);
+      } else {
+        const int idx = i - NPV, h2 = idx & 1, c = idx >> 1;
+        sacc[h2] = mfma_fp8_32x32x64(a, qop[c], c == 0 ? f32x16_t{} : sacc[h2], kE8M0One);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 template <int D, bool SPLIT>
-__global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, int32_t nqb) {
+__global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, int32_t qb_end,
+                                                          const int32_t* __restrict__ block_table) {
   using S = PrefillShape<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][S::TILE];   // [stage][K|V][key row]
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -115,8 +214,9 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   const int lg = lane >> 5;          // 32-lane half
 
   // ---- work item: (sequence, kv head) outer, q block descending (heaviest first) -----------
+  // the block grid covers q blocks [0, qb_end) of every (sequence, kv head)
   int64_t id = xcd_remap(blockIdx.x, gridDim.x);
-  const int qb = nqb - 1 - (int)(id % nqb); id /= nqb;
+  const int qb = qb_end - 1 - (int)(id % qb_end); id /= qb_end;
   const int h = (int)(id % p.hkv); id /= p.hkv;
   const int b = (int)id;
   const int G = p.group;
@@ -139,7 +239,6 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   const int wrl = min(wr0 + S::RW, nrows) - 1;
   const int wpf = L - ql + (wave_active ? wr0 : rlast) / G;
   const int wpl = L - ql + (wave_active ? wrl : rlast) / G;
-  const int wk_lo = W >= 1 ? max(0, wpf - W + 1) : 0;
   const int wfull_lo = W >= 1 ? wpl - W + 1 : 0;     // keys [wfull_lo, wpf] are visible to every row
   // this lane's row
   const int r = wr0 + lr;
@@ -176,12 +275,22 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
 #pragma unroll
   for (int t = 0; t < S::NDT; ++t) oacc[t] = f32x16_t{};
   float m_used = kNegInf, l_run = 0.f;
+  f32x16_t sacc[2];                 // S^T of the tile being processed (two 32-key halves)
+  i32x8_t pb = {}, pbl = {};        // P^T operands (hi and, for SPLIT, lo) of that tile
 
-  const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
+  // (read through a restrict pointer: the page ids come in with scalar loads, which leaves the
+  // vector memory counter to the tile loads alone)
+  const int32_t* bt = block_table + (int64_t)b * p.bt_stride;
   const uint8_t* kbase = p.k_cache + (int64_t)h * p.kv_stride_head;
   const uint8_t* vbase = p.v_cache + (int64_t)h * p.kv_stride_head;
   const int64_t sT = p.kv_stride_tok, sP = p.kv_stride_page;
   const int ps = p.page_size;
+
+  // ---- LDS stages --------------------------------------------------------------------------
+  // Three stages of [K tile | V tile]; tile x lives in stage (x - kt0) mod 3.
+  constexpr int SB = 2 * S::TILE;   // bytes per stage
+  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * SB];
+  const uint32_t lds_base = lds_address(lds);
 
   // ---- tile loader: HBM -> LDS directly (global_load_lds_dwordx4, 16 bytes per lane) ---------
   // A wave-wide instruction fills 64 consecutive 16-byte LDS slots (lane i -> slot i).  Key rows
@@ -192,17 +301,21 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   uint32_t loff[S::MAXI];
 #pragma unroll
   for (int t = 0; t < S::MAXI; ++t) {
-    const int ins = wave + S::NW * t;
+    const int ins = load_instruction<D>(wave, t);
     const int sl = (ins % S::SLOTS) * 64 + lane;
     const int row = sl / S::SLOTS, posn = sl % S::SLOTS;
     loff[t] = (uint32_t)(row * sT) + 16u * (uint32_t)(posn == S::NCH ? 0 : posn);
   }
-  auto issue = [&](int kt, int stage) {
-    const int j0 = kt * S::BK;
-    int pidx, slot0;
-    if (ps == S::BK) { pidx = kt; slot0 = 0; } else { pidx = j0 / ps; slot0 = j0 - pidx * ps; }
-    const int64_t tile_off = (int64_t)bt[pidx] * sP + (int64_t)slot0 * sT;
-    load_tile_to_lds<D>(kbase + tile_off, vbase + tile_off, loff, wave, &lds[stage][0][0]);
+  auto page_id = [&](int kt) __attribute__((always_inline)) -> int {
+    return bt[ps == S::BK ? kt : (kt * S::BK) / ps];
+  };
+  // issue this wave's loads of tile kt (page id page) into the stage at byte offset so
+  auto issue = [&](int so, int kt, int page) __attribute__((always_inline)) {
+    const int slot0 = ps == S::BK ? 0 : kt * S::BK - ((kt * S::BK) / ps) * ps;
+    const int64_t tile_off = (int64_t)page * sP + (int64_t)slot0 * sT;
+    const TileLoad tl{kbase + tile_off, vbase + tile_off, lds_base + (uint32_t)so};
+#pragma unroll
+    for (int k = 0; k < S::MAXI; ++k) tile_load_step<D>(tl, loff, wave, k);
   };
 
   // Row assignments.  MFMA row m of a 32-key half tile holds key kperm(m), which swaps bits 2
@@ -215,42 +328,33 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   const int tr_j = (lane & 15) >> 1;         // source row j (0..7) supplied by this lane
   const int tr_h = lane & 1;                 // 8-byte half of the 16-byte chunk
 
-  auto compute = [&](int kt, int stage) {
-    const uint8_t* ktile = lds[stage][0];
-    const uint8_t* vtile = lds[stage][1];
+  // S^T = K * Q^T for tile kt (K tile in stage st)
+  // S^T = K * Q^T for tile kt (K tile in stage st).  A operand row m holds key kperm(m).
+  const int k_lane = lane_offset(kperm(lr) * S::RS + 32 * lg);
+
+  // softmax of tile kt: mask (boundary tiles), lazy max, O rescale, P^T operands, running sum
+  auto softmax = [&](int kt) __attribute__((always_inline)) {
     const int j0 = kt * S::BK;
-    // S^T for the two 32-key halves of the tile
-    f32x16_t sacc[2];
+    const bool need_mask = !(j0 >= wfull_lo && j0 + S::BK - 1 <= wpf);
+    if (need_mask) {
+      // value i of this lane is S^T row 8*(i/4) + 4*lg + i%4, i.e. key kperm(that row); the
+      // visible keys of the row are (pos - W, pos]
+      // (the lane's 8*lg term is folded into the bounds so that jj is a constant)
+      const int jlo = (W >= 1 ? pos - W - j0 : -1 - j0) - 8 * lg, jhi = pos - j0 - 8 * lg;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      sacc[st] = f32x16_t{};
-      const int krow = 32 * st + kperm(lr);       // A operand row m holds key kperm(m)
-      const uint8_t* rowp = ktile + krow * S::RS + 32 * lg;
+      for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
-      for (int c = 0; c < S::KSTEP; ++c) {
-        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(rowp + 64 * c);
-        const u32x4_t y = *reinterpret_cast<const u32x4_t*>(rowp + 64 * c + 16);
-        const i32x8_t ka = {(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
-        sacc[st] = mfma_fp8_32x32x64(ka, qop[c], sacc[st], kE8M0One);
+        for (int i = 0; i < 16; ++i) {
+          const int jj = 32 * h2 + ((i >> 3) << 4) + (((i >> 2) & 1) << 2) + (i & 3);
+          sacc[h2][i] = (jj > jlo && jj <= jhi) ? sacc[h2][i] : kNegInf;
+        }
       }
     }
-    // mask (boundary tiles only) and tile max, on unscaled scores (the scale is positive)
-    const bool need_mask = !(j0 >= wfull_lo && j0 + S::BK - 1 <= wpf);
     float mxr = kNegInf;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v = sacc[st][i];
-        if (need_mask) {
-          // value i of this lane is S^T row 8*(i/4) + 4*lg + i%4, i.e. key kperm(that row)
-          const int j = j0 + 32 * st + ((i >> 3) << 4) + (lg << 3) + (((i >> 2) & 1) << 2) + (i & 3);
-          const bool vis = j <= pos && (W < 1 || j > pos - W);
-          v = vis ? v : kNegInf;
-          sacc[st][i] = v;
-        }
-        mxr = fmaxf(mxr, v);
-      }
+      for (int i = 0; i < 16; ++i) mxr = fmaxf(mxr, sacc[h2][i]);
     }
     mxr = fmaxf(mxr, __shfl_xor(mxr, 32, 64));
     const float mx = mxr * cs;
@@ -268,62 +372,114 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
       for (int t = 0; t < S::NDT; ++t) oacc[t] *= a;
     }
     const float neg_m = m_used == kNegInf ? 0.f : -m_used;
-    // P = exp2(s * cs - m), packed to E4M3 in the B-operand slot order (slot 16*st + i)
-    i32x8_t pb, pl = {};
+    // P = exp2(s * cs - m), packed to E4M3 in the B-operand slot order (slot 16*h2 + i)
     float lsum = 0.f;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         float e[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          e[k] = fast_exp2(__builtin_fmaf(sacc[st][4 * q4 + k], cs, neg_m));
+          e[k] = fast_exp2(__builtin_fmaf(sacc[h2][4 * q4 + k], cs, neg_m));
           lsum += e[k];
         }
         const uint32_t hi = pack4_e4m3(e[0], e[1], e[2], e[3]);
-        pb[4 * st + q4] = (int)hi;
+        pb[4 * h2 + q4] = (int)hi;
         if constexpr (SPLIT) {
           float back[4], rsd[4];
           unpack4_e4m3(hi, back);
 #pragma unroll
           for (int k = 0; k < 4; ++k) rsd[k] = (e[k] - back[k]) * 16.0f;
-          pl[4 * st + q4] = (int)pack4_e4m3(rsd[0], rsd[1], rsd[2], rsd[3]);
+          pbl[4 * h2 + q4] = (int)pack4_e4m3(rsd[0], rsd[1], rsd[2], rsd[3]);
         }
       }
     }
     l_run += lsum;
-    // O^T += V^T * P^T : for each 32-row d tile, gather 32 keys per lane with 4 transposing reads
-#pragma unroll
-    for (int dt = 0; dt < S::NDT; ++dt) {
-      const int col = 16 * dt + (D / 2) * tr_blk + 8 * tr_h;
-      i32x8_t va;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // slots 8q..8q+7 of group lg hold the 8 consecutive keys 32(q/2) + 16(q%2) + 8*lg + j
-        const int key = 32 * (q >> 1) + 16 * (q & 1) + 8 * lg + tr_j;
-        const uint8_t* src = vtile + key * S::RS + col;
-        const i32x2_t v2 = lds_read_tr8(src);
-        va[2 * q] = v2[0];
-        va[2 * q + 1] = v2[1];
-      }
-      oacc[dt] = mfma_fp8_32x32x64(va, pb, oacc[dt], kE8M0One);
-      if constexpr (SPLIT) oacc[dt] = mfma_fp8_32x32x64(va, pl, oacc[dt], kE8M0Sixteenth);
+    // P and the running sum are needed right here: without this the compiler sinks the whole
+    // exponential block past the barrier that follows, into the MFMA half of the period.
+    asm volatile("" ::"v"(pb), "v"(l_run));
+    if constexpr (SPLIT) asm volatile("" ::"v"(pbl));
+  };
+
+  // O^T += V^T * P^T with the V tile in stage st: per 32-row d tile, 4 transposing reads gather
+  // 32 keys per lane.  Slots 8q..8q+7 of lane group lg hold the 8 consecutive keys
+  // 32(q/2) + 16(q%2) + 8*lg + j, where j is the source row this lane supplies to the read.
+  const int v_lane = lane_offset((8 * lg + tr_j) * S::RS + (D / 2) * tr_blk + 8 * tr_h);
+  // MFMA work between two barriers: PV of the tile in stage so_v, then QK^T of the tile in stage
+  // so_k.  Every step runs both halves: where a step has no PV (before the first tile) P is
+  // still zero, and where it has no QK^T (after the last tile) S is not used again.
+  auto run_stream = [&](int so_v, int so_k) __attribute__((always_inline)) {
+    mfma_stream<D, SPLIT>(lds + (so_v + S::TILE + v_lane), lds + (so_k + k_lane), oacc, sacc, pb, pbl, qop);
+    // S is needed in this half period: keep the compiler from sinking the QK^T MFMAs past the
+    // barrier that may follow
+    asm volatile("" ::"v"(sacc[0]), "v"(sacc[1]));
+  };
+
+  // ---- main loop: two wave groups half a period apart -----------------------------------------
+  // Waves 0-3 (group A) and 4-7 (group B) share the SIMDs pairwise.  Per tile t:
+  //   group A:  softmax(t) | barrier | PV(t), QK(t+1)
+  //   group B:  PV(t-1), QK(t) | barrier | softmax(t)
+  // so one wave of each SIMD runs MFMAs while the other runs the softmax.  Before barrier t every
+  // wave's loads of tile t+1 have landed, and every wave has finished with tile t-1, whose stage
+  // then receives tile t+2.
+  const bool grpB = wave >= S::NW / 2;
+  // All of this wave's direct-to-LDS loads have landed.  Also a scheduling fence: the compiler may
+  // not move the softmax or MFMA work of one half period across the barrier into the other half,
+  // which would take away the overlap.
+  auto wait_loads = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  };
+  // The two groups run separate loops (wave-uniform branch) so that each keeps only its own
+  // values live across the barrier: S^T in group B, P^T in group A.  Both loops meet the same
+  // barriers: one before the first tile and one per tile.
+  // Stage byte offsets of tiles t - 1, t and t + 1 (tile t + 2 goes where t - 1 was).
+  int so_prev = 2 * SB, so_cur = 0, so_next = SB;
+  auto rotate = [&]() __attribute__((always_inline)) {
+    const int x = so_prev;
+    so_prev = so_cur;
+    so_cur = so_next;
+    so_next = x;
+  };
+  // page id of tile t + 2 while tile t is processed; the next one is read right after the loads
+  // of this one go out, a full period before it is needed
+  int page_ahead = kt0 + 2 <= kt1 ? page_id(kt0 + 2) : 0;
+  auto issue_ahead = [&](int t) __attribute__((always_inline)) {
+    if (t + 2 <= kt1) {
+      issue(so_prev, t + 2, page_ahead);
+      if (t + 3 <= kt1) page_ahead = page_id(t + 3);
     }
   };
 
-  // ---- main loop over key tiles (2-stage LDS ring, one barrier per tile) ---------------------
-  // Iteration kt: wait for this wave's loads of tile kt, barrier (every wave's loads of kt have
-  // landed and every wave has finished tile kt-1), start loading tile kt+1 into the stage that
-  // held tile kt-1, then compute tile kt.
-  issue(kt0, 0);
-  for (int kt = kt0; kt <= kt1; ++kt) {
-    const int stage = (kt - kt0) & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt < kt1) issue(kt + 1, stage ^ 1);
-    const int j0 = kt * S::BK;
-    if (wave_active && j0 + S::BK > wk_lo && j0 <= wpl) compute(kt, stage);
+  issue(so_cur, kt0, page_id(kt0));
+  if (kt0 + 1 <= kt1) issue(so_next, kt0 + 1, page_id(kt0 + 1));
+  wait_loads();
+  __syncthreads();   // tiles kt0 and kt0 + 1 are in LDS
+  // Every wave processes every tile of the block; tiles outside a wave's key range are fully
+  // masked for its rows (P = 0), which keeps the loop body one straight MFMA stream.
+  if (!grpB) {
+    run_stream(so_cur, so_cur);   // QK^T of the first tile (P is zero: the PV half adds nothing)
+    for (int t = kt0; t <= kt1; ++t) {
+      softmax(t);
+      wait_loads();
+      __syncthreads();
+      issue_ahead(t);
+      run_stream(so_cur, so_next);
+      rotate();
+    }
+  } else {
+    // one step past the last tile, which only finishes PV of the last tile
+    for (int t = kt0; t <= kt1 + 1; ++t) {
+      run_stream(t > kt0 ? so_prev : so_cur, so_cur);
+      if (t <= kt1) {
+        wait_loads();
+        __syncthreads();
+        issue_ahead(t);
+        softmax(t);
+      }
+      rotate();
+    }
   }
 
   // ---- epilogue ------------------------------------------------------------------------------
@@ -349,18 +505,21 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
 hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, hipStream_t stream) {
   const int G = p.group;
   const int64_t nqb = ((int64_t)p.max_seqlen_q * G + 255) / 256;
-  const int64_t grid = nqb * p.hkv * p.batch;
-  if (grid <= 0) return hipSuccess;
+  if (nqb <= 0 || p.hkv <= 0 || p.batch <= 0) return hipSuccess;
+  // A block runs in the split-P instance iff its first row sees fewer than kSplitPKeys keys, which
+  // needs its first row's token index below kSplitPKeys: only q blocks qb < nqb_split can.
+  const int64_t nqb_split = std::min<int64_t>(nqb, ((int64_t)(kSplitPKeys - 1) * G) / 256 + 1);
+  const int64_t grid = nqb * p.hkv * p.batch, grid_split = nqb_split * p.hkv * p.batch;
   if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidConfiguration;
-  // Every block index is launched twice, once per instance; each block runs in exactly one of
-  // them (decided by the key count its first row sees) and returns at once in the other.
-  const dim3 g((unsigned)grid), blk(512);
+  const dim3 blk(512);
   if (head_dim == 256) {
-    hipLaunchKernelGGL((prefill_fp8_kernel<256, false>), g, blk, 0, stream, p, (int32_t)nqb);
-    hipLaunchKernelGGL((prefill_fp8_kernel<256, true>), g, blk, 0, stream, p, (int32_t)nqb);
+    hipLaunchKernelGGL((prefill_fp8_kernel<256, false>), dim3((unsigned)grid), blk, 0, stream, p, (int32_t)nqb, p.block_table);
+    hipLaunchKernelGGL((prefill_fp8_kernel<256, true>), dim3((unsigned)grid_split), blk, 0, stream, p,
+                       (int32_t)nqb_split, p.block_table);
   } else {
-    hipLaunchKernelGGL((prefill_fp8_kernel<64, false>), g, blk, 0, stream, p, (int32_t)nqb);
-    hipLaunchKernelGGL((prefill_fp8_kernel<64, true>), g, blk, 0, stream, p, (int32_t)nqb);
+    hipLaunchKernelGGL((prefill_fp8_kernel<64, false>), dim3((unsigned)grid), blk, 0, stream, p, (int32_t)nqb, p.block_table);
+    hipLaunchKernelGGL((prefill_fp8_kernel<64, true>), dim3((unsigned)grid_split), blk, 0, stream, p,
+                       (int32_t)nqb_split, p.block_table);
   }
   return hipGetLastError();
 }

@@ -31,8 +31,14 @@ METRIC = "decode KV-read GB/s + prefill attention TFLOP/s, % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # dense FP8 MFMA
 BF16_PEAK_TFLOPS = 2500.0      # dense BF16 MFMA
-KERNEL_SOURCES = ["fp8_kv_cache_e4m3_amd/csrc/decode.hip", "fp8_kv_cache_e4m3_amd/csrc/device.h",
-                  "fp8_kv_cache_e4m3_amd/csrc/prefill.hip"]
+# sources each measured kernel is built from: a recorded traffic figure is used only while they
+# are unchanged
+KERNEL_SOURCES = {
+    "decode": ["fp8_kv_cache_e4m3_amd/csrc/decode.hip", "fp8_kv_cache_e4m3_amd/csrc/device.h",
+               "fp8_kv_cache_e4m3_amd/csrc/params.h"],
+    "prefill": ["fp8_kv_cache_e4m3_amd/csrc/prefill.hip", "fp8_kv_cache_e4m3_amd/csrc/device.h",
+                "fp8_kv_cache_e4m3_amd/csrc/params.h"],
+}
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -40,9 +46,9 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kind: str) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kind]:
         fp = os.path.join(ROOT, p)
         if os.path.exists(fp):
             h.update(open(fp, "rb").read())
@@ -228,10 +234,12 @@ def load_traffic(kernel_key):
         d = json.load(open(COUNTERS_FILE))
     except Exception:
         return None
-    if d.get("kernel_source_hash") != kernel_source_hash():
-        return None
     ent = d.get("kernels", {}).get(kernel_key)
-    return None if ent is None else ent.get("hbm_bytes_per_launch")
+    if ent is None or ent.get("source") not in KERNEL_SOURCES:
+        return None
+    if ent.get("source_hash") != kernel_source_hash(ent["source"]):
+        return None
+    return ent.get("hbm_bytes_per_launch")
 
 
 def main():

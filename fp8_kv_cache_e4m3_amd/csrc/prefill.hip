@@ -287,9 +287,10 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   const int ps = p.page_size;
 
   // ---- LDS stages --------------------------------------------------------------------------
-  // Three stages of [K tile | V tile]; tile x lives in stage (x - kt0) mod 3.
+  // Four stages of [K tile | V tile]; tile x lives in stage (x - kt0) mod 4.
   constexpr int SB = 2 * S::TILE;   // bytes per stage
-  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * SB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * SB];
+  auto stage_of = [&](int x) __attribute__((always_inline)) { return ((x - kt0) & 3) * SB; };
   const uint32_t lds_base = lds_address(lds);
 
   // ---- tile loader: HBM -> LDS directly (global_load_lds_dwordx4, 16 bytes per lane) ---------
@@ -417,70 +418,63 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   };
 
   // ---- main loop: two wave groups half a period apart -----------------------------------------
-  // Waves 0-3 (group A) and 4-7 (group B) share the SIMDs pairwise.  Per tile t:
-  //   group A:  softmax(t) | barrier | PV(t), QK(t+1)
-  //   group B:  PV(t-1), QK(t) | barrier | softmax(t)
-  // so one wave of each SIMD runs MFMAs while the other runs the softmax.  Before barrier t every
-  // wave's loads of tile t+1 have landed, and every wave has finished with tile t-1, whose stage
-  // then receives tile t+2.
+  // Waves 0-3 (group A) and 4-7 (group B) share the SIMDs pairwise.  Barrier t opens interval t:
+  //   group A:  loads of t+3 | PV(t), QK(t+1) | softmax(t+1)
+  //   group B:  softmax(t) | loads of t+3 | PV(t), QK(t+1)
+  // so one wave of each SIMD runs MFMAs while the other runs the softmax, and the two groups'
+  // load issue is staggered.  Only tiles t and t+1 are read in interval t; tile t+2 is landing
+  // (it is needed after barrier t+1) and tile t+3 goes into the stage tile t-1 has left, so a
+  // tile's loads have more than an interval to land.  Before each barrier a wave waits for all
+  // its loads but the ones of the interval that ends there.  Loads past the last tile fetch the
+  // last tile again into the free stage, which keeps the number of loads the same every interval.
   const bool grpB = wave >= S::NW / 2;
-  // All of this wave's direct-to-LDS loads have landed.  Also a scheduling fence: the compiler may
-  // not move the softmax or MFMA work of one half period across the barrier into the other half,
-  // which would take away the overlap.
+  // Before a barrier: the loads older than this interval's have landed.  Also a scheduling fence:
+  // the compiler may not move the softmax or MFMA work of one half period across the barrier into
+  // the other half, which would take away the overlap.
   auto wait_loads = []() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::MAXI));
   };
   // The two groups run separate loops (wave-uniform branch) so that each keeps only its own
   // values live across the barrier: S^T in group B, P^T in group A.  Both loops meet the same
   // barriers: one before the first tile and one per tile.
-  // Stage byte offsets of tiles t - 1, t and t + 1 (tile t + 2 goes where t - 1 was).
-  int so_prev = 2 * SB, so_cur = 0, so_next = SB;
-  auto rotate = [&]() __attribute__((always_inline)) {
-    const int x = so_prev;
-    so_prev = so_cur;
-    so_cur = so_next;
-    so_next = x;
-  };
-  // page id of tile t + 2 while tile t is processed; the next one is read right after the loads
-  // of this one go out, a full period before it is needed
-  int page_ahead = kt0 + 2 <= kt1 ? page_id(kt0 + 2) : 0;
-  auto issue_ahead = [&](int t) __attribute__((always_inline)) {
-    if (t + 2 <= kt1) {
-      issue(so_prev, t + 2, page_ahead);
-      if (t + 3 <= kt1) page_ahead = page_id(t + 3);
-    }
+  // page id of the tile interval I loads (tile min(I + 3, kt1)), read one interval ahead
+  int page_ahead = page_id(min(kt0 + 2, kt1));
+  auto interval_loads = [&](int I) __attribute__((always_inline)) {
+    issue(stage_of(I + 3), min(I + 3, kt1), page_ahead);
+    page_ahead = page_id(min(I + 4, kt1));
   };
 
-  issue(so_cur, kt0, page_id(kt0));
-  if (kt0 + 1 <= kt1) issue(so_next, kt0 + 1, page_id(kt0 + 1));
-  wait_loads();
-  __syncthreads();   // tiles kt0 and kt0 + 1 are in LDS
+  issue(stage_of(kt0), kt0, page_id(kt0));
+  issue(stage_of(kt0 + 1), min(kt0 + 1, kt1), page_id(min(kt0 + 1, kt1)));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();   // tiles kt0 and kt0 + 1 are in LDS; this opens interval kt0 - 1
+  interval_loads(kt0 - 1);
   // Every wave processes every tile of the block; tiles outside a wave's key range are fully
   // masked for its rows (P = 0), which keeps the loop body one straight MFMA stream.
   if (!grpB) {
-    run_stream(so_cur, so_cur);   // QK^T of the first tile (P is zero: the PV half adds nothing)
+    run_stream(stage_of(kt0), stage_of(kt0));   // QK^T of the first tile (P is zero: PV adds nothing)
     for (int t = kt0; t <= kt1; ++t) {
       softmax(t);
       wait_loads();
       __syncthreads();
-      issue_ahead(t);
-      run_stream(so_cur, so_next);
-      rotate();
+      interval_loads(t);                         // interval t
+      run_stream(stage_of(t), stage_of(t + 1));
     }
   } else {
-    // one step past the last tile, which only finishes PV of the last tile
+    // the stream at step t belongs to interval t - 1; one step past the last tile finishes PV
+    // of the last tile
     for (int t = kt0; t <= kt1 + 1; ++t) {
-      run_stream(t > kt0 ? so_prev : so_cur, so_cur);
+      run_stream(t > kt0 ? stage_of(t - 1) : stage_of(t), stage_of(t));
       if (t <= kt1) {
         wait_loads();
         __syncthreads();
-        issue_ahead(t);
         softmax(t);
+        interval_loads(t);                       // interval t
       }
-      rotate();
     }
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));       // nothing may land after the block ends
 
   // ---- epilogue ------------------------------------------------------------------------------
   l_run += __shfl_xor(l_run, 32, 64);

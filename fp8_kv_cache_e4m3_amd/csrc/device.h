@@ -58,26 +58,6 @@ __device__ __forceinline__ void transpose4x4_u8(uint32_t a0, uint32_t a1, uint32
 }
 
 // ---------------------------------------------------------------------------------------------
-// fp32 -> E4M3 code, round to nearest even, saturating at +-448, NaN -> 0x7F | sign.
-// Normal range: round the fp32 mantissa to 3 bits with the usual add-half-minus-one plus LSB
-// trick, then rebias the exponent (127 -> 7).  Below 2^-6 (E4M3 subnormals) scale by 2^9,
-// which is exact, and round to an integer 0..8 (8 is the smallest normal, code 0x08).
-// ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return 0x7fu | sign;           // NaN
-  if (a >= 0x43e00000u) return 0x7eu | sign;          // |y| >= 448 (and inf)
-  if (a < 0x3c800000u) {                              // |y| < 2^-6
-    const float f = __uint_as_float(a) * 512.0f;
-    return (uint32_t)__builtin_rintf(f) | sign;
-  }
-  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
-  return (r - (120u << 3)) | sign;
-}
-
-// ---------------------------------------------------------------------------------------------
 // MFMA wrappers (operand layouts measured on gfx950):
 //  16x16x32 bf16 / fp8 : lane l supplies row (A) or column (B) l%16 and 8 k-values for k-group
 //                        l/16; C lane l holds rows 4*(l/16)+i, column l%16.

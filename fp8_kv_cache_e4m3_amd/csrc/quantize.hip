@@ -2,36 +2,78 @@
 // sliding-window layers quantize Q before the FP8 forward).  Rule: one IEEE fp32 division by the
 // per-tensor descale, round to nearest even, saturate at +-448.  HBM-bound elementwise pass:
 // each thread moves 8 bf16 in (16 B) and 8 codes out (8 B).
+//
+// The fp32 quotient without a division per element: q = RN32(RN64(x * RN64(1 / descale))).  The
+// fp64 product is within about 2^-52 (relative) of x / descale.  For x with at most 24
+// significant bits (bf16 here) and an fp32 descale, x / descale is never exactly halfway between
+// two fp32 values.  It is also at least 2^-47 (relative) away from any halfway point: the
+// difference x - m * descale, for a halfway point m, is a nonzero multiple of a power of two
+// that small relative to x.  So the single rounding to fp32 lands where the correctly rounded
+// division does.  The E4M3 rounding then uses the converter (round to nearest even) on the
+// value clamped to +-448, which is the saturation of the rule.  The converter turns every NaN into
+// 0xFF, whereas the rule keeps the sign (0x7F | sign): a branch taken only where a lane holds a
+// NaN writes those codes.
 #include "device.h"
 #include "params.h"
 
 namespace fp8attn {
 
+// x / descale rounded to fp32 (see above), clamped to +-448 (a NaN comes out as a number here
+// and is fixed afterwards)
+__device__ __forceinline__ float quotient(float x, double rcp) {
+  const float q = (float)((double)x * rcp);
+  return __builtin_fminf(__builtin_fmaxf(q, -448.0f), 448.0f);
+}
+
+// CONTIG: Q rows (token, head) are back to back (head stride d, token stride heads * d), so the
+// input vector index is the output one and no index arithmetic is needed.
+template <bool CONTIG>
 __global__ void __launch_bounds__(256) quantize_q_kernel(const __bf16* __restrict__ q, int64_t nvec,
                                                          int32_t nheads, int32_t vec_per_head,
                                                          int64_t stride_tok, int64_t stride_head,
                                                          const float* __restrict__ q_descale,
                                                          uint8_t* __restrict__ out) {
   const float ds = q_descale ? q_descale[0] : 1.0f;
+  const double rcp = 1.0 / (double)ds;   // correctly rounded fp64 reciprocal
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
-    const int64_t c = v % vec_per_head;
-    const int64_t th = v / vec_per_head;
-    const int64_t hd = th % nheads;
-    const int64_t tok = th / nheads;
-    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(q + tok * stride_tok + hd * stride_head + c * 8);
-    uint32_t lo = 0, hi = 0;
+    int64_t src = v * 8;
+    if constexpr (!CONTIG) {
+      const int64_t c = v % vec_per_head;
+      const int64_t th = v / vec_per_head;
+      const int64_t hd = th % nheads;
+      const int64_t tok = th / nheads;
+      src = tok * stride_tok + hd * stride_head + c * 8;
+    }
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(q + src);
+    float x[8], y[8];
+    bool any_nan = false;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float x0 = __uint_as_float(w[k] << 16);
-      const float x1 = __uint_as_float(w[k] & 0xffff0000u);
-      const uint32_t c0 = f32_to_e4m3_rne_sat(x0 / ds);
-      const uint32_t c1 = f32_to_e4m3_rne_sat(x1 / ds);
-      const uint32_t pair = c0 | (c1 << 8);
-      if (k < 2) lo |= pair << (16 * k);
-      else hi |= pair << (16 * (k - 2));
+      x[2 * k] = __uint_as_float(w[k] << 16);
+      x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
     }
-    *reinterpret_cast<u32x2_t*>(out + v * 8) = u32x2_t{lo, hi};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      y[k] = quotient(x[k], rcp);
+      any_nan |= x[k] != x[k];
+    }
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+    if (any_nan) {   // rare: NaN codes keep the sign of the input
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (x[k] != x[k]) {
+          const uint32_t code = 0x7fu | ((__float_as_uint(x[k]) >> 24) & 0x80u);
+          const int sh = 8 * (k & 3);
+          if (k < 4) lo = (int)(((uint32_t)lo & ~(0xffu << sh)) | (code << sh));
+          else hi = (int)(((uint32_t)hi & ~(0xffu << sh)) | (code << sh));
+        }
+      }
+    }
+    *reinterpret_cast<u32x2_t*>(out + v * 8) = u32x2_t{(uint32_t)lo, (uint32_t)hi};
   }
 }
 
@@ -43,9 +85,15 @@ hipError_t launch_quantize_q(const void* q, int64_t ntok, int32_t nheads, int32_
   if (nvec == 0) return hipSuccess;
   int64_t blocks = (nvec + 255) / 256;
   if (blocks > 256 * 64) blocks = 256 * 64;
-  hipLaunchKernelGGL(quantize_q_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     reinterpret_cast<const __bf16*>(q), nvec, nheads, vph, stride_tok, stride_head,
-                     q_descale, reinterpret_cast<uint8_t*>(out));
+  const bool contig = stride_head == d && stride_tok == (int64_t)nheads * d;
+  if (contig)
+    hipLaunchKernelGGL(quantize_q_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const __bf16*>(q), nvec, nheads, vph, stride_tok, stride_head, q_descale,
+                       reinterpret_cast<uint8_t*>(out));
+  else
+    hipLaunchKernelGGL(quantize_q_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const __bf16*>(q), nvec, nheads, vph, stride_tok, stride_head, q_descale,
+                       reinterpret_cast<uint8_t*>(out));
   return hipGetLastError();
 }
 

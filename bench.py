@@ -78,9 +78,11 @@ def visible_keys(w):
     return total
 
 
-def algo_bytes(w):
+def algo_bytes(w, fused=True):
+    """Bytes the attention call must move: visible K/V (1 byte each), Q (bf16 when the call
+    quantizes it or takes it unquantized, E4M3 codes when quantized beforehand) and bf16 out."""
     kv = visible_keys(w) * w.num_kv_heads * w.head_dim * 2          # K and V, 1 byte each
-    qb = w.total_q * w.num_q_heads * w.head_dim * (1 if w.q_dtype == "e4m3" else 2)
+    qb = w.total_q * w.num_q_heads * w.head_dim * (1 if (w.q_dtype == "e4m3" and not fused) else 2)
     ob = w.total_q * w.num_q_heads * w.head_dim * 2
     return kv + qb + ob, kv
 
@@ -93,19 +95,24 @@ def algo_flops(w):
 # GPU steps
 # ------------------------------------------------------------------------------------------
 class Runner:
-    def __init__(self, w, entry):
+    """One input set.  For E4M3 workloads the step takes bf16 Q: by default the attention call
+    quantizes it in-kernel (one launch); with fused=False a separate quantize call writes the
+    codes first (two launches)."""
+    def __init__(self, w, entry, fused=True):
         import torch
         import fp8_kv_cache_e4m3_amd as fa
         self.fa, self.torch, self.w, self.entry = fa, torch, w, entry
         self.out = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
         self.lse = torch.empty((w.total_q, w.num_q_heads), dtype=torch.float32, device="cuda")
         self.qcodes = None
-        if w.q_dtype == "e4m3":
+        if w.q_dtype == "e4m3" and not fused:
             self.qcodes = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=torch.uint8, device="cuda")
-        q = self.qcodes if w.q_dtype == "e4m3" else w.q
+        q = self.qcodes if self.qcodes is not None else w.q
         self.args = fa.make_args(q, w.k_pool, w.v_pool, w.block_table, w.cu_seqlens_q, w.seqlens_k,
-                                 w.max_seqlen_q, w.max_seqlen_k, w.q_descale, w.k_descale, w.v_descale,
-                                 0.0, w.window, True, self.out, self.lse)
+                                 w.max_seqlen_q, w.max_seqlen_k,
+                                 w.q_descale if w.q_dtype == "e4m3" else None, w.k_descale, w.v_descale,
+                                 0.0, w.window, True, self.out, self.lse,
+                                 quantize_q=(w.q_dtype == "e4m3" and fused))
         self.ws = None
         self.splits = 1
         if entry == "decode":
@@ -133,11 +140,11 @@ class Runner:
         assert st == 0, fa.fp8attn_last_error()
 
 
-def time_workload(make, entry, nsets, steps, warmup, label):
+def time_workload(make, entry, nsets, steps, warmup, label, fused=True):
     """Returns dict with ms_per_step (whole step) and kernel_ms (attention call only, HIP events)."""
     import torch
     t0 = time.time()
-    runners = [Runner(make(seed), entry) for seed in range(nsets)]
+    runners = [Runner(make(seed), entry, fused) for seed in range(nsets)]
     torch.cuda.synchronize()
     log(f"[bench] {label}: {nsets} input sets ready in {time.time() - t0:.1f}s; splits={runners[0].splits}")
     stream = torch.cuda.current_stream()
@@ -252,7 +259,11 @@ def main():
     ap.add_argument("--profile-pass", default=None,
                     choices=["swa_decode", "full_decode", "spec_verify", "swa_prefill"],
                     help="short run for rocprofv3 counter passes: one workload plus a 1 GiB device copy")
+    ap.add_argument("--separate-quantize", action="store_true",
+                    help="quantize Q with its own call before attention (two launches per step) instead of "
+                         "inside the attention kernel")
     args = ap.parse_args()
+    fused = not args.separate_quantize
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -281,18 +292,19 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
         make, entry = makers[args.profile_pass]
-        time_workload(make, entry, 2, args.steps, args.warmup, f"{args.profile_pass} (profile pass)")
+        time_workload(make, entry, 2, args.steps, args.warmup, f"{args.profile_pass} (profile pass)", fused)
         return
 
     main = time_workload(lambda s: wl.swa_decode(device="cuda", seed=100 + s), "decode", nsets, args.steps,
-                         args.warmup, "sliding-window decode")
+                         args.warmup, "sliding-window decode", fused)
     w = main["w"]
-    total_b, kv_b = algo_bytes(w)
+    total_b, kv_b = algo_bytes(w, fused)
     value = total_b / (main["ms_per_step"] * 1e-3) / 1e9
     achieved = total_b / (main["kernel_ms"] * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic("decode_swa"),
-            "kernel": "decode_kernel<true,256> (sliding-window decode, one split)",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic("decode_swa") if fused else None,
+            "kernel": f"decode_kernel<{2 if fused else 1},256> (sliding-window decode, one split, "
+                      f"{'bf16 Q quantized in-kernel' if fused else 'E4M3 Q codes'})",
             "algorithmic_bytes_per_launch": total_b}
 
     extra = {}
@@ -303,9 +315,9 @@ def main():
             ("swa_prefill", lambda s: wl.swa_prefill(device="cuda", seed=400 + s), "prefill", 2, "mfma"),
         ]
         for name, make, entry, ns, bound in specs:
-            r = time_workload(make, entry, ns, max(5, args.steps // 5), 2, name)
+            r = time_workload(make, entry, ns, max(5, args.steps // 5), 2, name, fused)
             ww = r["w"]
-            tb, kvb = algo_bytes(ww)
+            tb, kvb = algo_bytes(ww, fused)
             fl = algo_flops(ww)
             e = {"workload": ww.name, "ms_per_step": round(r["ms_per_step"], 4),
                  "attention_ms": round(r["kernel_ms"], 4), "splits": r["splits"],
@@ -331,7 +343,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "window": w.window, "kv_len": "uniform[1024,8192]", "page": 64,
-                   "input_sets": nsets, "splits": main["splits"], "step": "quantize_q + decode_paged"},
+                   "input_sets": nsets, "splits": main["splits"],
+                   "step": "decode_paged (bf16 Q quantized in-kernel)" if fused else "quantize_q + decode_paged"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "extra": extra,

@@ -39,7 +39,9 @@ fp8attn_status hip_fail(const char* where, hipError_t e) {
   return fail(FP8ATTN_ERR_HIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
 }
 
-const char* dtype_name(int32_t t) { return t == FP8ATTN_BF16 ? "bf16" : t == FP8ATTN_E4M3 ? "e4m3" : "unknown"; }
+const char* dtype_name(int32_t t) {
+  return t == FP8ATTN_BF16 ? "bf16" : t == FP8ATTN_E4M3 ? "e4m3" : t == FP8ATTN_BF16_TO_E4M3 ? "bf16->e4m3" : "unknown";
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -60,14 +62,14 @@ int cu_count() {
 // Supported (q dtype, head dim) pairs: native FP8 at head dim 256 (vLLM PR #63139, Overview) and
 // BF16 Q at head dim 512 (vLLM PR #60372, Overview), plus head dim 64 for both as a small case.
 bool supported_combo(int32_t q_dtype, int32_t d) {
-  if (q_dtype == FP8ATTN_E4M3) return d == 64 || d == 256;
+  if (q_dtype == FP8ATTN_E4M3 || q_dtype == FP8ATTN_BF16_TO_E4M3) return d == 64 || d == 256;
   if (q_dtype == FP8ATTN_BF16) return d == 64 || d == 512;
   return false;
 }
 
 fp8attn_status validate_attn(const char* fn, const fp8attn_attn_args* a, bool decode) {
   if (!a) return fail(FP8ATTN_ERR_INVALID_ARG, "%s: args is NULL", fn);
-  if (a->q_dtype != FP8ATTN_BF16 && a->q_dtype != FP8ATTN_E4M3)
+  if (a->q_dtype != FP8ATTN_BF16 && a->q_dtype != FP8ATTN_E4M3 && a->q_dtype != FP8ATTN_BF16_TO_E4M3)
     return fail(FP8ATTN_ERR_INVALID_ARG, "%s: unknown q_dtype %d", fn, a->q_dtype);
   if (a->reserved0 != 0 || a->reserved1 != 0)
     return fail(FP8ATTN_ERR_INVALID_ARG, "%s: reserved fields must be 0", fn);
@@ -80,7 +82,7 @@ fp8attn_status validate_attn(const char* fn, const fp8attn_attn_args* a, bool de
   if (!supported_combo(a->q_dtype, a->head_dim))
     return fail(FP8ATTN_ERR_UNSUPPORTED,
                 "%s: unsupported combination q=%s k=e4m3 v=e4m3 head_size=%d head_size_v=%d "
-                "(supported: q=e4m3 with head_size 64 or 256; q=bf16 with head_size 64 or 512; "
+                "(supported: q=e4m3 or bf16->e4m3 with head_size 64 or 256; q=bf16 with head_size 64 or 512; "
                 "k/v always e4m3 with head_size_v == head_size)",
                 fn, dtype_name(a->q_dtype), a->head_dim, a->head_dim);
   if (a->causal != 1)
@@ -116,7 +118,7 @@ fp8attn_status validate_attn(const char* fn, const fp8attn_attn_args* a, bool de
   if (!a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->cu_seqlens_q || !a->seqlens_k || !a->out)
     return fail(FP8ATTN_ERR_INVALID_ARG, "%s: a required pointer (q, k_cache, v_cache, block_table, cu_seqlens_q, "
                 "seqlens_k, out) is NULL", fn);
-  const int64_t qelt = a->q_dtype == FP8ATTN_BF16 ? 2 : 1;
+  const int64_t qelt = a->q_dtype == FP8ATTN_E4M3 ? 1 : 2;
   if (!aligned(a->q, 16) || (a->q_stride_tok * qelt) % 16 != 0 || (a->q_stride_head * qelt) % 16 != 0 ||
       a->q_stride_tok < 0 || a->q_stride_head < 0)
     return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: q must be 16-byte aligned with 16-byte-multiple strides", fn);
@@ -281,7 +283,7 @@ fp8attn_status fp8attn_decode_paged(const fp8attn_attn_args* args, int32_t num_s
     p.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
                                           round_up((size_t)pl.splits * rows * args->head_dim * sizeof(float)));
   }
-  hipError_t e = fp8attn::launch_decode(p, args->q_dtype == FP8ATTN_E4M3, args->head_dim, pl.grid, stream);
+  hipError_t e = fp8attn::launch_decode(p, args->q_dtype, args->head_dim, pl.grid, stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   if (pl.splits > 1) {
     e = fp8attn::launch_combine(p.part_o, p.part_lse, pl.splits, args->total_q, args->num_q_heads, args->head_dim,
@@ -298,8 +300,8 @@ fp8attn_status fp8attn_prefill_varlen(const fp8attn_attn_args* args, hipStream_t
   if (args->total_q == 0 || args->batch == 0) return ok();
   fp8attn::AttnParams p = make_params(args);
   hipError_t e;
-  if (args->q_dtype == FP8ATTN_E4M3) {
-    e = fp8attn::launch_prefill_fp8(p, args->head_dim, stream);
+  if (args->q_dtype == FP8ATTN_E4M3 || args->q_dtype == FP8ATTN_BF16_TO_E4M3) {
+    e = fp8attn::launch_prefill_fp8(p, args->head_dim, args->q_dtype == FP8ATTN_BF16_TO_E4M3, stream);
   } else {
     // BF16 queries: the split-KV kernel over 16-row query tiles, one split per tile.
     const int G = args->num_q_heads / args->num_kv_heads;
@@ -309,7 +311,7 @@ fp8attn_status fp8attn_prefill_varlen(const fp8attn_attn_args* args, hipStream_t
     const int64_t grid = (int64_t)args->num_kv_heads * args->batch * p.row_groups;
     if (grid >= (int64_t)1 << 31)
       return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: grid of %lld blocks is too large", fn, (long long)grid);
-    e = fp8attn::launch_decode(p, false, args->head_dim, grid, stream);
+    e = fp8attn::launch_decode(p, fp8attn::kQBf16, args->head_dim, grid, stream);
   }
   if (e != hipSuccess) return hip_fail(fn, e);
   return ok();

@@ -4,9 +4,11 @@
 // pairs of one kv head, token-major) over the keys of one KV split, on a paged E4M3 cache with
 // per-tensor descales (vLLM PR #60372, Overview/Claims; prhub digest of vLLM PR #48666, Key
 // code), for both variants:
-//   QFP8 = true : E4M3 Q codes (vLLM PR #63139, Overview), QK^T on the FP8 MFMA;
-//   QFP8 = false: BF16 Q, K dequantized in registers (exact: E4M3 values are bf16 values),
-//                 QK^T on the BF16 MFMA.
+//   QM = kQE4M3   : E4M3 Q codes (vLLM PR #63139, Overview), QK^T on the FP8 MFMA;
+//   QM = kQBf16E4M3: bf16 Q quantized to E4M3 as the kernel loads it, with the same arithmetic
+//                   as fp8attn_quantize_q (identical codes), then the same FP8 path;
+//   QM = kQBf16   : BF16 Q, K dequantized in registers (exact: E4M3 values are bf16 values),
+//                   QK^T on the BF16 MFMA.
 // PV runs on the BF16 MFMA in both variants: V bytes are dequantized exactly to bf16 and P is
 // rounded once to bf16.  Decode is HBM-bound, so the cheaper FP8 PV would not move the time but
 // would cost accuracy on short rows.
@@ -95,8 +97,9 @@ struct QRegs<true, D> { uint64_t q[2 * DecodeShape<D>::KCH]; };
 template <int D>
 struct QRegs<false, D> { bf16x8_t q[2 * DecodeShape<D>::KCH]; };
 
-template <bool QFP8, int D>
+template <int QM, int D>
 __global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
+  constexpr bool QFP8 = QM != kQBf16;   // QK^T on the FP8 MFMA
   using S = DecodeShape<D>;
   using T = DecodeTune<QFP8, D>;
   constexpr int NBUF = T::NBUF;
@@ -149,12 +152,13 @@ __global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
 
   const float kd = p.k_descale ? p.k_descale[b * p.ds_stride_b + h * p.ds_stride_h] : 1.0f;
   const float vd = p.v_descale ? p.v_descale[b * p.ds_stride_b + h * p.ds_stride_h] : 1.0f;
-  float cscale = p.scale_log2 * kd;
-  if constexpr (QFP8) cscale *= p.q_descale ? p.q_descale[0] : 1.0f;
+  const float qd = QFP8 && p.q_descale ? p.q_descale[0] : 1.0f;
+  const float cscale = p.scale_log2 * kd * qd;
 
   // ---- Q^T operand (rows on lane columns) ---------------------------------------------------
   QRegs<QFP8, D> qr;
-  if constexpr (QFP8) {
+  u32x4_t qraw[QM == kQBf16E4M3 ? 2 * S::KCH : 1];
+  if constexpr (QM == kQE4M3) {
     const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)(t0 + tok) * p.q_stride_tok +
                         (int64_t)hq * p.q_stride_head + 16 * grp;
 #pragma unroll
@@ -162,6 +166,16 @@ __global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
       u32x4_t w = rvalid ? *reinterpret_cast<const u32x4_t*>(qp + 64 * c) : u32x4_t{0, 0, 0, 0};
       qr.q[2 * c] = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
       qr.q[2 * c + 1] = (uint64_t)w[2] | ((uint64_t)w[3] << 32);
+    }
+  } else if constexpr (QM == kQBf16E4M3) {
+    // the same 16 d values per k-chunk as above, read as bf16 here and quantized once the first
+    // units' loads are in flight (below); a row past the end reads the clamped row
+    const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)(t0 + tok) * p.q_stride_tok +
+                       (int64_t)hq * p.q_stride_head + 16 * grp;
+#pragma unroll
+    for (int c = 0; c < S::KCH; ++c) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) qraw[2 * c + hf] = *reinterpret_cast<const u32x4_t*>(qp + 64 * c + 8 * hf);
     }
   } else {
     const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)(t0 + tok) * p.q_stride_tok +
@@ -261,6 +275,15 @@ __global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
     const int ulast = su1 - 1;
 #pragma unroll
     for (int k = 0; k < NBUF; ++k) issue(buf[k], min(u0 + 4 * k, ulast));
+    if constexpr (QM == kQBf16E4M3) {
+      // quantize bf16 Q with the arithmetic of the stand-alone quantize call (identical codes)
+      const double rcp = 1.0 / (double)qd;
+#pragma unroll
+      for (int i = 0; i < 2 * S::KCH; ++i) {
+        const u32x2_t e = quantize8_bf16_e4m3(qraw[i], rcp);
+        qr.q[i] = rvalid ? ((uint64_t)e[0] | ((uint64_t)e[1] << 32)) : 0;
+      }
+    }
     for (int u = u0; u < su1; u += 4 * NBUF) {
 #pragma unroll
       for (int k = 0; k < NBUF; ++k) {
@@ -344,16 +367,19 @@ __global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
   }
 }
 
-hipError_t launch_decode(const AttnParams& p, bool q_e4m3, int head_dim, int64_t grid,
+hipError_t launch_decode(const AttnParams& p, int q_mode, int head_dim, int64_t grid,
                          hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   const dim3 g((unsigned)grid), blk(256);
-  if (q_e4m3) {
-    if (head_dim == 256) hipLaunchKernelGGL((decode_kernel<true, 256>), g, blk, 0, stream, p);
-    else hipLaunchKernelGGL((decode_kernel<true, 64>), g, blk, 0, stream, p);
+  if (q_mode == kQE4M3) {
+    if (head_dim == 256) hipLaunchKernelGGL((decode_kernel<kQE4M3, 256>), g, blk, 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel<kQE4M3, 64>), g, blk, 0, stream, p);
+  } else if (q_mode == kQBf16E4M3) {
+    if (head_dim == 256) hipLaunchKernelGGL((decode_kernel<kQBf16E4M3, 256>), g, blk, 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel<kQBf16E4M3, 64>), g, blk, 0, stream, p);
   } else {
-    if (head_dim == 512) hipLaunchKernelGGL((decode_kernel<false, 512>), g, blk, 0, stream, p);
-    else hipLaunchKernelGGL((decode_kernel<false, 64>), g, blk, 0, stream, p);
+    if (head_dim == 512) hipLaunchKernelGGL((decode_kernel<kQBf16, 512>), g, blk, 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel<kQBf16, 64>), g, blk, 0, stream, p);
   }
   return hipGetLastError();
 }

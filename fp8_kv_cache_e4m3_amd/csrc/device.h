@@ -58,6 +58,53 @@ __device__ __forceinline__ void transpose4x4_u8(uint32_t a0, uint32_t a1, uint32
 }
 
 // ---------------------------------------------------------------------------------------------
+// Q quantization to E4M3, shared by fp8attn_quantize_q and the attention kernels that take bf16
+// Q for the native-FP8 path (both give identical codes).  The rule: fp32 quotient q / descale,
+// round to nearest even, saturate at +-448, NaN -> 0x7F | sign.  The fp32 quotient is
+// RN32(RN64(x * RN64(1 / descale))), which equals the correctly rounded division for every x
+// with at most 24 significant bits; the argument is given where fp8attn_quantize_q is defined.
+// rcp is RN64(1 / descale).
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float q_quotient_clamped(float x, double rcp) {
+  const float q = (float)((double)x * rcp);
+  return __builtin_fminf(__builtin_fmaxf(q, -448.0f), 448.0f);   // a NaN is fixed afterwards
+}
+// the 8 bf16 of a 16-byte word -> 8 E4M3 codes (element i in byte i of the two dwords).
+// The clamp maps a NaN quotient to a finite value, so NaN inputs are patched afterwards.  The test
+// for them is a wave-wide ballot (one compare per element, OR-ed in scalar registers), and the
+// patch is a wave-uniform branch that real data never takes.
+__device__ __forceinline__ u32x2_t quantize8_bf16_e4m3(const u32x4_t w, double rcp) {
+  float x[8], y[8];
+  uint64_t nan_lanes = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(w[k] << 16);
+    x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    y[k] = q_quotient_clamped(x[k], rcp);
+    nan_lanes |= __builtin_amdgcn_ballot_w64(x[k] != x[k]);
+  }
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+  if (nan_lanes != 0) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (x[k] != x[k]) {
+        const uint32_t code = 0x7fu | ((__float_as_uint(x[k]) >> 24) & 0x80u);
+        const int sh = 8 * (k & 3);
+        if (k < 4) lo = (int)(((uint32_t)lo & ~(0xffu << sh)) | (code << sh));
+        else hi = (int)(((uint32_t)hi & ~(0xffu << sh)) | (code << sh));
+      }
+    }
+  }
+  return u32x2_t{(uint32_t)lo, (uint32_t)hi};
+}
+
+// ---------------------------------------------------------------------------------------------
 // MFMA wrappers (operand layouts measured on gfx950):
 //  16x16x32 bf16 / fp8 : lane l supplies row (A) or column (B) l%16 and 8 k-values for k-group
 //                        l/16; C lane l holds rows 4*(l/16)+i, column l%16.

@@ -40,16 +40,22 @@ struct AttnParams {
   float* part_lse;                             // fp32 [S, total_q, hq]
 };
 
+// How the kernels receive Q (values of fp8attn_dtype)
+constexpr int kQBf16 = 0;       // bf16 values, BF16 MFMA with K/V dequantized
+constexpr int kQE4M3 = 1;       // E4M3 codes, FP8 MFMA
+constexpr int kQBf16E4M3 = 2;   // bf16 values quantized to E4M3 on load, FP8 MFMA
+
 hipError_t launch_quantize_q(const void* q, int64_t ntok, int32_t nheads, int32_t d,
                              int64_t stride_tok, int64_t stride_head, const float* q_descale,
                              void* out, hipStream_t stream);
 
 // Split-KV paged attention over 16-row query tiles.  grid = row_groups * batch * S * hkv.
-hipError_t launch_decode(const AttnParams& p, bool q_e4m3, int head_dim, int64_t grid,
+hipError_t launch_decode(const AttnParams& p, int q_mode, int head_dim, int64_t grid,
                          hipStream_t stream);
 
 // Native-FP8 prefill: 256 query rows per block, 64-key tiles through LDS.  head_dim 64 or 256.
-hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, hipStream_t stream);
+// q_bf16: Q comes in bf16 and is quantized on load (q mode kQBf16E4M3), else E4M3 codes.
+hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, bool q_bf16, hipStream_t stream);
 
 hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t S, int64_t total_q,
                           int32_t hq, int32_t d, void* out, int64_t out_stride_tok,

@@ -203,7 +203,9 @@ __device__ __forceinline__ void mfma_stream(const uint8_t* vp, const uint8_t* kp
   }
 }
 
-template <int D, bool SPLIT>
+// QBF16: Q comes in bf16 and is quantized to E4M3 as it is loaded, with the same arithmetic as
+// fp8attn_quantize_q (identical codes); otherwise Q holds E4M3 codes.
+template <int D, bool SPLIT, bool QBF16>
 __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, int32_t qb_end,
                                                           const int32_t* __restrict__ block_table) {
   using S = PrefillShape<D>;
@@ -257,7 +259,7 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
 
   // ---- Q^T operand: lane (row lr, half lg) holds Q[row][64c + 32lg .. +32] per k-step c -------
   i32x8_t qop[S::KSTEP];
-  {
+  if constexpr (!QBF16) {
     const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)(t0 + tok) * p.q_stride_tok +
                         (int64_t)hq * p.q_stride_head + 32 * lg;
 #pragma unroll
@@ -270,6 +272,7 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
       qop[c] = i32x8_t{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)bb[0], (int)bb[1], (int)bb[2], (int)bb[3]};
     }
   }
+  // (bf16 Q is loaded and quantized further down, once the first tiles' loads are in flight)
 
   f32x16_t oacc[S::NDT];
 #pragma unroll
@@ -447,6 +450,31 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
 
   issue(stage_of(kt0), kt0, page_id(kt0));
   issue(stage_of(kt0 + 1), min(kt0 + 1, kt1), page_id(min(kt0 + 1, kt1)));
+  if constexpr (QBF16) {
+    // The same 32 d values per k-step as the E4M3 codes, read as bf16 and quantized here, with
+    // the arithmetic of the stand-alone quantize call (identical codes).  Every load is issued
+    // before the first conversion so that their latencies overlap each other and the tile loads
+    // above; a row past the end reads the clamped row and is zeroed.
+    const double rcp = 1.0 / (double)qd;   // (qd was read before the tile loads: no wait here)
+    const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)(t0 + tok) * p.q_stride_tok +
+                       (int64_t)hq * p.q_stride_head + 32 * lg;
+    u32x4_t qw[S::KSTEP][4];
+#pragma unroll
+    for (int c = 0; c < S::KSTEP; ++c) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qw[c][k] = *reinterpret_cast<const u32x4_t*>(qp + 64 * c + 8 * k);
+    }
+#pragma unroll
+    for (int c = 0; c < S::KSTEP; ++c) {
+      u32x2_t e[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) e[k] = quantize8_bf16_e4m3(qw[c][k], rcp);
+      qop[c] = i32x8_t{(int)e[0][0], (int)e[0][1], (int)e[1][0], (int)e[1][1],
+                       (int)e[2][0], (int)e[2][1], (int)e[3][0], (int)e[3][1]};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qop[c][k] = rvalid ? qop[c][k] : 0;
+    }
+  }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();   // tiles kt0 and kt0 + 1 are in LDS; this opens interval kt0 - 1
   interval_loads(kt0 - 1);
@@ -496,7 +524,17 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
     p.lse[(int64_t)(t0 + tok) * p.hq + hq] = l_run > 0.f ? (m_used + fast_log2(l_run)) * kLn2 : kNegInf;
 }
 
-hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, hipStream_t stream) {
+template <int D, bool QBF16>
+static void launch_prefill_pair(const AttnParams& p, int64_t grid, int64_t nqb, int64_t grid_split,
+                                int64_t nqb_split, hipStream_t stream) {
+  const dim3 blk(512);
+  hipLaunchKernelGGL((prefill_fp8_kernel<D, false, QBF16>), dim3((unsigned)grid), blk, 0, stream, p, (int32_t)nqb,
+                     p.block_table);
+  hipLaunchKernelGGL((prefill_fp8_kernel<D, true, QBF16>), dim3((unsigned)grid_split), blk, 0, stream, p,
+                     (int32_t)nqb_split, p.block_table);
+}
+
+hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, bool q_bf16, hipStream_t stream) {
   const int G = p.group;
   const int64_t nqb = ((int64_t)p.max_seqlen_q * G + 255) / 256;
   if (nqb <= 0 || p.hkv <= 0 || p.batch <= 0) return hipSuccess;
@@ -505,15 +543,12 @@ hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, hipStream_t str
   const int64_t nqb_split = std::min<int64_t>(nqb, ((int64_t)(kSplitPKeys - 1) * G) / 256 + 1);
   const int64_t grid = nqb * p.hkv * p.batch, grid_split = nqb_split * p.hkv * p.batch;
   if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidConfiguration;
-  const dim3 blk(512);
   if (head_dim == 256) {
-    hipLaunchKernelGGL((prefill_fp8_kernel<256, false>), dim3((unsigned)grid), blk, 0, stream, p, (int32_t)nqb, p.block_table);
-    hipLaunchKernelGGL((prefill_fp8_kernel<256, true>), dim3((unsigned)grid_split), blk, 0, stream, p,
-                       (int32_t)nqb_split, p.block_table);
+    if (q_bf16) launch_prefill_pair<256, true>(p, grid, nqb, grid_split, nqb_split, stream);
+    else launch_prefill_pair<256, false>(p, grid, nqb, grid_split, nqb_split, stream);
   } else {
-    hipLaunchKernelGGL((prefill_fp8_kernel<64, false>), dim3((unsigned)grid), blk, 0, stream, p, (int32_t)nqb, p.block_table);
-    hipLaunchKernelGGL((prefill_fp8_kernel<64, true>), dim3((unsigned)grid_split), blk, 0, stream, p,
-                       (int32_t)nqb_split, p.block_table);
+    if (q_bf16) launch_prefill_pair<64, true>(p, grid, nqb, grid_split, nqb_split, stream);
+    else launch_prefill_pair<64, false>(p, grid, nqb, grid_split, nqb_split, stream);
   }
   return hipGetLastError();
 }

@@ -18,13 +18,6 @@
 
 namespace fp8attn {
 
-// x / descale rounded to fp32 (see above), clamped to +-448 (a NaN comes out as a number here
-// and is fixed afterwards)
-__device__ __forceinline__ float quotient(float x, double rcp) {
-  const float q = (float)((double)x * rcp);
-  return __builtin_fminf(__builtin_fmaxf(q, -448.0f), 448.0f);
-}
-
 // CONTIG: Q rows (token, head) are back to back (head stride d, token stride heads * d), so the
 // input vector index is the output one and no index arithmetic is needed.
 template <bool CONTIG>
@@ -46,34 +39,7 @@ __global__ void __launch_bounds__(256) quantize_q_kernel(const __bf16* __restric
       src = tok * stride_tok + hd * stride_head + c * 8;
     }
     const u32x4_t w = *reinterpret_cast<const u32x4_t*>(q + src);
-    float x[8], y[8];
-    bool any_nan = false;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[2 * k] = __uint_as_float(w[k] << 16);
-      x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      y[k] = quotient(x[k], rcp);
-      any_nan |= x[k] != x[k];
-    }
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
-    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
-    if (any_nan) {   // rare: NaN codes keep the sign of the input
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (x[k] != x[k]) {
-          const uint32_t code = 0x7fu | ((__float_as_uint(x[k]) >> 24) & 0x80u);
-          const int sh = 8 * (k & 3);
-          if (k < 4) lo = (int)(((uint32_t)lo & ~(0xffu << sh)) | (code << sh));
-          else hi = (int)(((uint32_t)hi & ~(0xffu << sh)) | (code << sh));
-        }
-      }
-    }
-    *reinterpret_cast<u32x2_t*>(out + v * 8) = u32x2_t{(uint32_t)lo, (uint32_t)hi};
+    *reinterpret_cast<u32x2_t*>(out + v * 8) = quantize8_bf16_e4m3(w, rcp);
   }
 }
 

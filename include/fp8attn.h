@@ -57,7 +57,8 @@ typedef enum fp8attn_status {
 
 typedef enum fp8attn_dtype {
   FP8ATTN_BF16 = 0,              /* bfloat16 */
-  FP8ATTN_E4M3 = 1               /* OCP float8 E4M3 (torch.float8_e4m3fn), stored as bytes */
+  FP8ATTN_E4M3 = 1,              /* OCP float8 E4M3 (torch.float8_e4m3fn), stored as bytes */
+  FP8ATTN_BF16_TO_E4M3 = 2       /* bfloat16 Q quantized to E4M3 inside the call (q only) */
 } fp8attn_dtype;
 
 /*
@@ -67,6 +68,9 @@ typedef enum fp8attn_dtype {
 typedef struct fp8attn_attn_args {
   /* Queries [total_q, num_q_heads, head_dim], head_dim contiguous.
    * q_dtype FP8ATTN_E4M3: codes from fp8attn_quantize_q (native FP8 variant, [63139]).
+   * q_dtype FP8ATTN_BF16_TO_E4M3: bf16 values that the call quantizes with q_descale exactly
+   *   as fp8attn_quantize_q would (identical codes, so identical results), then the native
+   *   FP8 variant; it saves the separate quantization pass.  Head dims as for E4M3.
    * q_dtype FP8ATTN_BF16: bf16 values (K/V dequantized in-kernel, [48666]).            */
   const void* q;
   int32_t q_dtype;
@@ -94,8 +98,8 @@ typedef struct fp8attn_attn_args {
   /* Descales: device fp32.  NULL means 1.0 (a unit scale needs no tensor).  K/V descales may
    * vary per (sequence, kv head): element [b*descale_stride_b + h*descale_stride_h]; strides
    * 0,0 give one per-tensor value ([60372] Claims: normalized descale layouts; [48666]).
-   * q_descale is one per-tensor value; it must be NULL when q_dtype is BF16, because that
-   * path takes unquantized Q ([48666] Implementation item 3).                                 */
+   * q_descale is one per-tensor value (used by E4M3 and BF16_TO_E4M3); it must be NULL when
+   * q_dtype is BF16, because that path takes unquantized Q ([48666] Implementation item 3).                                 */
   const float* q_descale;
   const float* k_descale;
   const float* v_descale;
@@ -126,9 +130,9 @@ fp8attn_status fp8attn_quantize_q(const void* q_bf16, int64_t num_tokens, int32_
 
 /*
  * Paged attention for varlen batches of new tokens (prefill / chunked prefill), any q_len.
- * Supported: (q_dtype E4M3, head_dim 64 or 256) and (q_dtype BF16, head_dim 64 or 512); K/V are
- * E4M3 with V head dim equal to head_dim ([60372] review thread).  Writes args->out and, if
- * non-NULL, args->lse.
+ * Supported: (q_dtype E4M3 or BF16_TO_E4M3, head_dim 64 or 256) and (q_dtype BF16, head_dim 64
+ * or 512); K/V are E4M3 with V head dim equal to head_dim ([60372] review thread).  Writes
+ * args->out and, if non-NULL, args->lse.
  */
 fp8attn_status fp8attn_prefill_varlen(const fp8attn_attn_args* args, hipStream_t stream);
 

@@ -67,14 +67,17 @@ def oracle_run(w: wl.Workload, tokens=None, window=None, softmax_scale=None):
 
 
 def gpu_run(w: wl.Workload, entry="decode", num_splits=0, window=None, softmax_scale=0.0, want_lse=True,
-            out=None, q_codes=None):
+            out=None, q_codes=None, fused_q=False):
     """Run the HIP path.  Returns (o float64 [T,Hq,d], lse [T,Hq] or None, q codes (uint8 numpy) or
-    None, splits used)."""
+    None, splits used).  With fused_q an e4m3 workload hands bf16 Q to the attention call, which
+    quantizes it itself (no codes are returned then)."""
     import fp8_kv_cache_e4m3_amd as fa
     dev = torch.device("cuda")
     wd = w.to(dev)
     codes = None
-    if w.q_dtype == "e4m3":
+    if w.q_dtype == "e4m3" and fused_q:
+        q, qd = wd.q, wd.q_descale
+    elif w.q_dtype == "e4m3":
         q = fa.fp8attn_quantize_q(wd.q, wd.q_descale) if q_codes is None else q_codes
         codes = q.cpu().numpy()
         qd = wd.q_descale
@@ -82,7 +85,7 @@ def gpu_run(w: wl.Workload, entry="decode", num_splits=0, window=None, softmax_s
         q, qd = wd.q, None
     win = w.window if window is None else window
     kw = dict(q_descale=qd, k_descale=wd.k_descale, v_descale=wd.v_descale, softmax_scale=softmax_scale,
-              window=win, want_lse=want_lse, out=out)
+              window=win, want_lse=want_lse, out=out, quantize_q=fused_q)
     args = (q, wd.k_pool, wd.v_pool, wd.block_table, wd.cu_seqlens_q, wd.seqlens_k, w.max_seqlen_q,
             w.max_seqlen_k)
     splits = 1

@@ -75,6 +75,7 @@ def _status(a, fn="prefill"):
     ({"causal": 0}, fa.ERR_UNSUPPORTED, ["non-causal", "q=bf16", "head_size=512"]),
     ({"head_dim": 256}, fa.ERR_UNSUPPORTED, ["q=bf16", "k=e4m3", "v=e4m3", "head_size=256", "head_size_v=256"]),
     ({"q_dtype": fa.E4M3, "head_dim": 512}, fa.ERR_UNSUPPORTED, ["q=e4m3", "head_size=512"]),
+    ({"q_dtype": fa.BF16_TO_E4M3, "head_dim": 512}, fa.ERR_UNSUPPORTED, ["q=bf16->e4m3", "head_size=512"]),
     ({"head_dim": 128}, fa.ERR_UNSUPPORTED, ["head_size=128"]),
     ({"page_size": 32}, fa.ERR_UNSUPPORTED, ["page_size 32", "multiple of 64"]),
     ({"page_size": 96}, fa.ERR_UNSUPPORTED, ["page_size 96"]),
@@ -100,6 +101,18 @@ def test_rejections(fn, change, status, words):
     msg = fa.fp8attn_last_error()
     for w in words:
         assert w in msg, (w, msg)
+
+
+@pytest.mark.parametrize("fn", ["prefill", "decode"])
+@pytest.mark.parametrize("q_dtype", [fa.E4M3, fa.BF16_TO_E4M3])
+@pytest.mark.parametrize("head_dim", [64, 256])
+def test_quantized_q_modes_pass_validation(fn, q_dtype, head_dim):
+    # Both quantized-query modes are accepted at head_size 64 and 256, with or without a
+    # q_descale; an empty batch then returns OK without touching the device.
+    for qd in (0, 0x1000):
+        a, keep = _valid_args(q_dtype=q_dtype, head_dim=head_dim, q_descale=qd, batch=0, total_q=0)
+        st = _status(a, fn)
+        assert st == fa.OK, (st, fa.fp8attn_last_error())
 
 
 def test_decode_rejects_long_query():

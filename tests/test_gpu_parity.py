@@ -107,6 +107,49 @@ def test_workload_full_size_sampled(name, entry, nsample):
 
 
 # ------------------------------------------------------------------------------------------
+# bf16 Q quantized inside the attention kernels: the same codes as the separate quantize
+# call, so the outputs equal the two-call path bit for bit (and meet the oracle bar)
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name,scale,entry,splits", [
+    ("tiny", None, "prefill", 0),
+    ("tiny", None, "decode", 0),
+    ("swa_decode", 0.25, "decode", 0),
+    ("swa_decode", 0.25, "decode", 3),
+    ("multi_token_d256", None, "decode", 0),
+    ("multi_token_d64", None, "decode", 2),
+    ("swa_prefill", 1 / 32, "prefill", 0),
+    ("ragged_d64", None, "prefill", 0),
+])
+def test_fused_q_quantization(name, scale, entry, splits):
+    if name == "tiny":
+        w = wl.tiny("e4m3")
+    elif name == "multi_token_d256":     # several query tokens per sequence, GQA 8:1, window
+        w = wl.custom("e4m3", 256, 16, 2, 300, [700, 65, 1500], [4, 16, 1], seed=21)
+    elif name == "multi_token_d64":
+        w = wl.custom("e4m3", 64, 8, 1, -1, [129, 64, 999], [3, 7, 16], seed=22)
+    elif name == "ragged_d64":           # prefill with ragged query lengths and tails
+        w = wl.custom("e4m3", 64, 4, 2, 100, [300, 37, 513], [300, 20, 257], seed=23)
+    else:
+        w = wl.BY_NAME[name](device="cpu", scale=scale)
+    assert w.q_dtype == "e4m3"
+    log(f"[case] fused-q {w.name} entry={entry} splits={splits}")
+    o2, l2, _, s2 = gpu_run(w, entry, num_splits=splits)
+    o1, l1, codes, s1 = gpu_run(w, entry, num_splits=splits, fused_q=True)
+    assert codes is None and s1 == s2
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    o_ref, l_ref, _ = oracle_run(w)
+    compare(o1, o_ref, l1, l_ref, label=f"fused-q {w.name} S={s1}")
+
+
+def test_fused_q_full_size_swa_decode():
+    w = wl.BY_NAME["swa_decode"](device="cuda")
+    log(f"[case] fused-q full-size {w.name}")
+    o2, l2, _, _ = gpu_run(w, "decode")
+    o1, l1, _, _ = gpu_run(w, "decode", fused_q=True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ------------------------------------------------------------------------------------------
 # split-KV: every split count meets the bar; one split needs no workspace
 # ------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 0, 1000])

@@ -30,6 +30,8 @@
 
 namespace fp8attn {
 
+constexpr float kLazyMax = 8.0f;   // log2 units: the running max moves by more than 2^8 or not at all
+
 template <int D>
 struct DecodeShape {
   static constexpr int kKeys = 16;                    // keys per unit
@@ -234,18 +236,25 @@ __global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
     }
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mx = max_over_groups(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    // Lazy running max: it moves only when a unit exceeds it by more than 2^8, so P <= 256 and
+    // the O rescale (64 accumulators) is rare after the first unit.  A row whose max is still
+    // -inf has O = 0 and l = 0, so its first move needs no rescale of O.
+    const bool grow = mx > m_run + kLazyMax;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));   // 1 where not grown
+      l_run *= alpha;
+      if (__any(grow && m_run != kNegInf)) {
+#pragma unroll
+        for (int t = 0; t < S::NT; ++t) oacc[t] *= alpha;
+      }
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
     float pv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(sv[i] - m_use);
-    l_run = l_run * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
-    m_run = m_new;
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int t = 0; t < S::NT; ++t) oacc[t] *= alpha;
-    }
+    l_run += (pv[0] + pv[1]) + (pv[2] + pv[3]);
     const bf16x4_t pb = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
     // O^T += V^T * P^T
 #pragma unroll

@@ -152,10 +152,22 @@ __global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
     return;
   }
 
-  const float kd = p.k_descale ? p.k_descale[b * p.ds_stride_b + h * p.ds_stride_h] : 1.0f;
-  const float vd = p.v_descale ? p.v_descale[b * p.ds_stride_b + h * p.ds_stride_h] : 1.0f;
-  const float qd = QFP8 && p.q_descale ? p.q_descale[0] : 1.0f;
+  const int64_t dsi = (int64_t)b * p.ds_stride_b + (int64_t)h * p.ds_stride_h;
+  const float kd = p.k_descale ? load_uniform(p.k_descale, dsi) : 1.0f;
+  const float vd = p.v_descale ? load_uniform(p.v_descale, dsi) : 1.0f;
+  const float qd = QFP8 && p.q_descale ? load_uniform(p.q_descale, 0) : 1.0f;
   const float cscale = p.scale_log2 * kd * qd;
+
+  // Page ids of the split's keys: lane i holds the id of page pg_base + i (clamped to the split's
+  // last page), refreshed 64 pages at a time.  A unit's page id is then a register read
+  // (v_readlane) instead of a memory load on the path to the unit's loads.  Units are issued in
+  // increasing order, so the window only moves forward.  (Read before Q, so that waiting for it
+  // does not wait for the Q loads.)
+  const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
+  const int ps = p.page_size;
+  const int pg_last = ((su1 - 1) * 16) / ps;
+  int pg_base = (su0 * 16) / ps;
+  int pg_vec = bt[min(pg_base + lane, pg_last)];
 
   // ---- Q^T operand (rows on lane columns) ---------------------------------------------------
   QRegs<QFP8, D> qr;
@@ -194,34 +206,46 @@ __global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
   for (int t = 0; t < S::NT; ++t) oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
 
-  const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
   const uint8_t* kbase = p.k_cache + (int64_t)h * p.kv_stride_head;
   const uint8_t* vbase = p.v_cache + (int64_t)h * p.kv_stride_head;
   const int64_t sT = p.kv_stride_tok, sP = p.kv_stride_page;
-  const int ps = p.page_size;
+  auto page_of = [&](int u) __attribute__((always_inline)) -> int {
+    const int pi = (u * 16) / ps;
+    if (pi - pg_base >= 64) {   // wave-uniform; only splits longer than 64 pages get here
+      pg_base = pi;
+      pg_vec = bt[min(pi + lane, pg_last)];
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    return __builtin_amdgcn_readlane(pg_vec, pi - pg_base);
+  };
 
-  auto issue = [&](UnitRegs<D>& ur, int u) {
+  auto issue = [&](UnitRegs<D>& ur, int u) __attribute__((always_inline)) {
     const int j0 = u * 16;
-    const int64_t page = bt[j0 / ps];
+    const int64_t page = page_of(u);
     const int slot0 = j0 % ps;
     load_unit<D, T::NT>(ur, kbase + page * sP, vbase + page * sP, sT, slot0, col, grp);
   };
 
-  auto compute = [&](const UnitRegs<D>& ur, int u) {
-    // S^T tile: rows = 16 keys of the unit, columns = 16 query rows
+  // S^T tile of a unit: rows = its 16 keys, columns = the 16 query rows
+  auto qk = [&](const u32x4_t (&kk)[S::KCH]) __attribute__((always_inline)) -> f32x4_t {
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < S::KCH; ++c) {
       if constexpr (QFP8) {
-        const uint64_t k0 = (uint64_t)ur.k[c][0] | ((uint64_t)ur.k[c][1] << 32);
-        const uint64_t k1 = (uint64_t)ur.k[c][2] | ((uint64_t)ur.k[c][3] << 32);
+        const uint64_t k0 = (uint64_t)kk[c][0] | ((uint64_t)kk[c][1] << 32);
+        const uint64_t k1 = (uint64_t)kk[c][2] | ((uint64_t)kk[c][3] << 32);
         sacc = mfma_fp8_16x16x32(k0, qr.q[2 * c], sacc);
         sacc = mfma_fp8_16x16x32(k1, qr.q[2 * c + 1], sacc);
       } else {
-        sacc = mfma_bf16_16x16x32(e4m3x8_to_bf16(ur.k[c][0], ur.k[c][1]), qr.q[2 * c], sacc);
-        sacc = mfma_bf16_16x16x32(e4m3x8_to_bf16(ur.k[c][2], ur.k[c][3]), qr.q[2 * c + 1], sacc);
+        sacc = mfma_bf16_16x16x32(e4m3x8_to_bf16(kk[c][0], kk[c][1]), qr.q[2 * c], sacc);
+        sacc = mfma_bf16_16x16x32(e4m3x8_to_bf16(kk[c][2], kk[c][3]), qr.q[2 * c + 1], sacc);
       }
     }
+    return sacc;
+  };
+
+  // mask, online softmax update, P^T operand of unit u (lane (row, g) holds keys 4g..4g+3)
+  auto softmax = [&](const f32x4_t sacc, int u) __attribute__((always_inline)) -> bf16x4_t {
     float sv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sv[i] = sacc[i] * cscale;
@@ -255,8 +279,14 @@ __global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(sv[i] - m_use);
     l_run += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-    const bf16x4_t pb = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
-    // O^T += V^T * P^T
+    return bf16x4_t{(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
+  };
+
+  // O^T += V^T * P^T with V in registers (lane (col, g) holds bytes col*CW.. of keys 4g..4g+3):
+  // a 4x4 byte transpose gives, per O^T tile t, row col <-> d = 16 col + t (d256) or the
+  // analogous interleave (d64, d512)
+  auto compute = [&](const UnitRegs<D>& ur, int u) __attribute__((always_inline)) {
+    const bf16x4_t pb = softmax(qk(ur.k), u);
 #pragma unroll
     for (int blk = 0; blk < S::VBLK; ++blk) {
 #pragma unroll
@@ -274,14 +304,14 @@ __global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
   };
 
   // ---- main loop: this wave takes units su0+wave, su0+wave+4, ... --------------------------
-  // A ring of NBUF register buffers: NBUF - 1 units stay in flight while one is computed.  Every
-  // trip issues the same loads (indices past the end are clamped to the split's last unit, an
-  // in-bounds re-read that hits L2), so the compiler can wait for exactly the oldest unit
-  // instead of draining every outstanding load.
+  const int u0 = su0 + wave;
+  const int ulast = su1 - 1;
   {
+    // A ring of NBUF register buffers: NBUF - 1 units stay in flight while one is computed.
+    // Every trip issues the same loads (indices past the end are clamped to the split's last
+    // unit, an in-bounds re-read that hits L2), so the compiler can wait for exactly the oldest
+    // unit instead of draining every outstanding load.
     UnitRegs<D> buf[NBUF];
-    const int u0 = su0 + wave;
-    const int ulast = su1 - 1;
 #pragma unroll
     for (int k = 0; k < NBUF; ++k) issue(buf[k], min(u0 + 4 * k, ulast));
     if constexpr (QM == kQBf16E4M3) {

@@ -14,9 +14,49 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector memory operations of
+// this wave are outstanding and leaves the other counters unconstrained
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+
+// A uniform read of read-only data through the constant address space: a scalar load, which
+// waits on lgkmcnt and leaves the vector memory counter to the streaming loads.
+__device__ __forceinline__ float load_uniform(const float* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) float*)p)[i];
+}
+
+// ---------------------------------------------------------------------------------------------
+// Direct-to-LDS loads, issued from inline assembly on purpose: the compiler then does not track
+// them, and the kernel alone orders them against the LDS reads (explicit vmcnt waits before the
+// barrier that publishes a tile).  When the compiler tracks them itself, it cannot prove that
+// reads of one stage are independent of loads into another across loop iterations and drains
+// all loads in flight before every read.
+// ---------------------------------------------------------------------------------------------
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ i32x2_t lds_read_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(p));
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// One wave-wide direct-to-LDS load: lane i copies the 16 bytes at gbase + voff (voff per lane)
+// to LDS address lds_dst + 16 i.  M0 holds the LDS address; gfx9 needs one wait state between an
+// SALU write of M0 and the load that reads it.  M0 is not otherwise live in these kernels.
+__device__ __forceinline__ void lds_dma16(const uint8_t* gbase, uint32_t voff, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(lds_dst)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // ---------------------------------------------------------------------------------------------
 // E4M3 -> bf16, exact: every E4M3 value is a bf16 value.  gfx950's v_cvt_scalef32_pk_bf16_fp8

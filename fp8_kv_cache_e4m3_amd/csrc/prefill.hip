@@ -38,7 +38,6 @@ namespace fp8attn {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kSplitPKeys = 512;
 constexpr int kE8M0One = 127;        // E8M0 scale 2^0
@@ -48,10 +47,6 @@ constexpr float kLazyMax = 8.0f;
 __device__ __forceinline__ f32x16_t mfma_fp8_32x32x64(const i32x8_t& a, const i32x8_t& b, f32x16_t c,
                                                       int scale_b) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kE8M0One, 0, scale_b);
-}
-
-__device__ __forceinline__ i32x2_t lds_read_tr8(const uint8_t* p) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(p));
 }
 
 // four fp32 -> four E4M3 bytes (round to nearest even; inputs are in [0, 448])
@@ -100,29 +95,6 @@ struct PrefillShape {
   static_assert(D == 64 || D == 256, "head dim");
 };
 
-// LDS byte address of a pointer into a __shared__ array
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// One wave-wide direct-to-LDS load: lane i copies the 16 bytes at gbase + voff (voff per lane)
-// to LDS address lds_dst + 16 i.  It is issued from inline assembly on purpose: the compiler
-// then does not track it, and the kernel alone orders these loads against the LDS reads (every
-// wave waits for its own loads, vmcnt(0), before the barrier that publishes a tile).  When the
-// compiler tracks them itself, it cannot prove that reads of one stage are independent of loads
-// into another across loop iterations and drains all loads in flight before every read.
-// M0 holds the LDS address; gfx9 needs one wait state between an SALU write of M0 and the load
-// that reads it.  M0 is not otherwise live in these kernels.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(const uint8_t* gbase, uint32_t voff, uint32_t lds_dst) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(gbase), "s"(lds_dst)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
 // Direct-to-LDS loads of one K and one V tile: D/16 + 1 16-byte slots per key row (the pad slot
 // gets a copy of the row's first chunk), 64 lanes per instruction, 2 * (D/16 + 1) instructions
 // per tile.  Wave w issues instructions w, w + 8, ...; every wave issues MAXI of them, a wave
@@ -147,9 +119,6 @@ __device__ __forceinline__ void tile_load_step(const TileLoad& tl, const uint32_
   const int blk = ins % S::SLOTS;
   lds_dma16(which ? tl.v_src : tl.k_src, loff[k], tl.lds_stage + (uint32_t)(which * S::TILE + blk * 1024));
 }
-// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector memory operations of
-// this wave are outstanding and leaves the other counters unconstrained
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // The MFMA work of one wave between two barriers: O^T += V^T * P^T for one tile (PV) and then
 // S^T = K * Q^T for another (QK).  Operands are read from LDS two MFMAs ahead of their use, in a

@@ -56,40 +56,51 @@ __device__ __forceinline__ T stream_load(const T* p) {
   else return *p;
 }
 
+// Per-lane byte offsets inside a unit, the same for every unit: K row col, bytes 16 grp (+ 64 c);
+// V rows 4 grp + i, bytes col * CW (+ 16 CW blk).  A unit's loads are then a uniform base (page
+// plus first slot) plus these 32-bit offsets: the SGPR-base form of the global loads.
+struct UnitOffsets {
+  uint32_t k;
+  uint32_t v[4];
+};
+
 template <int D, bool NT>
-__device__ __forceinline__ void load_unit(UnitRegs<D>& ur, const uint8_t* __restrict__ kpage,
-                                          const uint8_t* __restrict__ vpage, int64_t sT, int slot0,
-                                          int col, int grp) {
+__device__ __forceinline__ void load_unit(UnitRegs<D>& ur, const uint8_t* __restrict__ kunit,
+                                          const uint8_t* __restrict__ vunit, const UnitOffsets& off) {
   using S = DecodeShape<D>;
-  const uint8_t* kp = kpage + (int64_t)(slot0 + col) * sT + 16 * grp;
 #pragma unroll
-  for (int c = 0; c < S::KCH; ++c) ur.k[c] = stream_load<NT>(reinterpret_cast<const u32x4_t*>(kp + 64 * c));
+  for (int c = 0; c < S::KCH; ++c)
+    ur.k[c] = stream_load<NT>(reinterpret_cast<const u32x4_t*>(kunit + off.k + 64 * c));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint8_t* vp = vpage + (int64_t)(slot0 + 4 * grp + i) * sT + col * S::CW;
 #pragma unroll
     for (int blk = 0; blk < S::VBLK; ++blk) {
+      const uint8_t* vp = vunit + off.v[i] + blk * 16 * S::CW;
       if constexpr (S::CW == 16) {
-        const u32x4_t w = stream_load<NT>(reinterpret_cast<const u32x4_t*>(vp + blk * 16 * S::CW));
+        const u32x4_t w = stream_load<NT>(reinterpret_cast<const u32x4_t*>(vp));
         ur.v[i][blk][0] = w[0];
         ur.v[i][blk][1] = w[1];
         ur.v[i][blk][2] = w[2];
         ur.v[i][blk][3] = w[3];
       } else {
-        ur.v[i][blk][0] = stream_load<NT>(reinterpret_cast<const uint32_t*>(vp + blk * 16 * S::CW));
+        ur.v[i][blk][0] = stream_load<NT>(reinterpret_cast<const uint32_t*>(vp));
       }
     }
   }
 }
 
-// Per-variant tuning (measured on MI355X): register ring depth and non-temporal K/V loads.
-// Deeper rings need more than 256 registers at d256 (one wave per SIMD instead of two), which
-// measured slower; at d512 a third buffer spills.  Non-temporal loads help the d256 stream
-// (+5%) and hurt the split d512 stream (-11%).
+// Per-variant tuning (measured on MI355X, sliding-window decode, cold K/V).  Two units in
+// flight per wave; deeper register rings (3 or 4 units, which fit at two waves per SIMD) were
+// slower, as were rings staged through LDS with direct-to-LDS loads.  A plain gather with this
+// access pattern (256-byte row slices, 16 rows per instruction) tops out near 47 us for the
+// 269 MB, against about 50 us for the kernel.  Non-temporal loads help the d256 stream (+4%)
+// and hurt the split d512 stream (-11%).
 template <bool QFP8, int D>
 struct DecodeTune {
   static constexpr int NBUF = 2;
   static constexpr bool NT = QFP8 && D == 256;
+  // d256 runs two waves per SIMD: the register budget is 256 per wave
+  static constexpr int MIN_WAVES = D == 256 ? 2 : 1;
 };
 
 template <bool QFP8, int D>
@@ -100,7 +111,8 @@ template <int D>
 struct QRegs<false, D> { bf16x8_t q[2 * DecodeShape<D>::KCH]; };
 
 template <int QM, int D>
-__global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
+__global__ void __launch_bounds__(256)
+    __attribute__((amdgpu_waves_per_eu(DecodeTune<QM != kQBf16, D>::MIN_WAVES))) decode_kernel(const AttnParams p) {
   constexpr bool QFP8 = QM != kQBf16;   // QK^T on the FP8 MFMA
   using S = DecodeShape<D>;
   using T = DecodeTune<QFP8, D>;
@@ -219,11 +231,14 @@ __global__ void __launch_bounds__(256) decode_kernel(const AttnParams p) {
     return __builtin_amdgcn_readlane(pg_vec, pi - pg_base);
   };
 
+  UnitOffsets uoff;
+  uoff.k = (uint32_t)(col * sT) + 16u * (uint32_t)grp;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) uoff.v[i] = (uint32_t)((4 * grp + i) * sT) + (uint32_t)(col * S::CW);
   auto issue = [&](UnitRegs<D>& ur, int u) __attribute__((always_inline)) {
     const int j0 = u * 16;
-    const int64_t page = page_of(u);
-    const int slot0 = j0 % ps;
-    load_unit<D, T::NT>(ur, kbase + page * sP, vbase + page * sP, sT, slot0, col, grp);
+    const int64_t unit = page_of(u) * sP + (int64_t)(j0 % ps) * sT;
+    load_unit<D, T::NT>(ur, kbase + unit, vbase + unit, uoff);
   };
 
   // S^T tile of a unit: rows = its 16 keys, columns = the 16 query rows

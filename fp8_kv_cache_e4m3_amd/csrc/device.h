@@ -81,20 +81,20 @@ __device__ __forceinline__ bf16x4_t e4m3x4_to_bf16(uint32_t w) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// 4x4 byte transpose: in row k holds bytes x[k][0..3]; out e holds x[0..3][e].
-// Written with shifts and masks; the compiler turns them into v_perm_b32.
+// 4x4 byte transpose: in row k holds bytes x[k][0..3]; out e holds x[0..3][e].  Eight
+// v_perm_b32: interleave the bytes of rows (0,1) and (2,3), then pair up their 16-bit halves.
+// (v_perm_b32 selector byte 0..3 picks a byte of the second source, 4..7 of the first.)
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ void transpose4x4_u8(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
                                                 uint32_t& t0, uint32_t& t1, uint32_t& t2, uint32_t& t3) {
-  // interleave bytes of (a0,a1) and (a2,a3)
-  const uint32_t p01l = (a0 & 0xffu) | ((a1 & 0xffu) << 8) | ((a0 & 0xff00u) << 8) | ((a1 & 0xff00u) << 16);
-  const uint32_t p01h = ((a0 >> 16) & 0xffu) | (((a1 >> 16) & 0xffu) << 8) | ((a0 >> 24) << 16) | ((a1 >> 24) << 24);
-  const uint32_t p23l = (a2 & 0xffu) | ((a3 & 0xffu) << 8) | ((a2 & 0xff00u) << 8) | ((a3 & 0xff00u) << 16);
-  const uint32_t p23h = ((a2 >> 16) & 0xffu) | (((a3 >> 16) & 0xffu) << 8) | ((a2 >> 24) << 16) | ((a3 >> 24) << 24);
-  t0 = (p01l & 0xffffu) | (p23l << 16);
-  t1 = (p01l >> 16) | (p23l & 0xffff0000u);
-  t2 = (p01h & 0xffffu) | (p23h << 16);
-  t3 = (p01h >> 16) | (p23h & 0xffff0000u);
+  const uint32_t p01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u);   // a0.0 a1.0 a0.1 a1.1
+  const uint32_t p01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);   // a0.2 a1.2 a0.3 a1.3
+  const uint32_t p23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
+  const uint32_t p23h = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+  t0 = __builtin_amdgcn_perm(p23l, p01l, 0x05040100u);
+  t1 = __builtin_amdgcn_perm(p23l, p01l, 0x07060302u);
+  t2 = __builtin_amdgcn_perm(p23h, p01h, 0x05040100u);
+  t3 = __builtin_amdgcn_perm(p23h, p01h, 0x07060302u);
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -188,9 +188,12 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Split-KV plan from host-known maxima only (no device reads, so the call is capturable).
-// Automatic mode picks the split count from the work per block, with no fixed cap (vLLM PR
-// #60372, Claims): about 2 MiB of K+V per block, then more splits until the grid holds at
-// least two blocks per compute unit, never fewer than 4 units (64 keys) per split.
+// Automatic mode picks the split count with no fixed cap (vLLM PR #60372, Claims): just enough
+// splits for the grid to fill the chip once (the blocks that fit at once: two per compute unit
+// at head dim <= 256, one at 512, four at 64), with at least 32 units (512 keys) per split.
+// Every block pays a Q load, a merge of its waves and, when split, a partial write, so fewer and
+// longer blocks measured faster on every decode workload here (B64 d512 full decode: 1.15 ms at
+// the former 16 splits, 1.04 ms at one; spec-verify 1.36 ms at 15, 1.11 ms at one).
 DecodePlan plan_decode(const fp8attn_attn_args* a, int32_t requested) {
   DecodePlan pl{};
   const int G = a->num_q_heads / a->num_kv_heads;
@@ -203,11 +206,10 @@ DecodePlan plan_decode(const fp8attn_attn_args* a, int32_t requested) {
   if (requested > 0) {
     S = requested;
   } else {
-    const int64_t bytes_per_unit = 16 * 2 * (int64_t)a->head_dim;
-    const int64_t cus = cu_count();
-    int64_t ups = std::max<int64_t>(4, (2 << 20) / bytes_per_unit);
-    S = (pl.max_units + ups - 1) / ups;
-    while (items * S < 2 * (int64_t)cus && (pl.max_units + S) / (S + 1) >= 4) ++S;
+    const int64_t per_cu = a->head_dim > 256 ? 1 : a->head_dim > 64 ? 2 : 4;
+    const int64_t resident = (int64_t)cu_count() * per_cu;
+    S = (resident + items - 1) / items;
+    S = std::min<int64_t>(S, std::max<int64_t>(1, pl.max_units / 32));
   }
   S = std::max<int64_t>(1, std::min<int64_t>(S, pl.max_units));
   pl.units_per_split = (int32_t)((pl.max_units + S - 1) / S);

@@ -28,13 +28,15 @@ Modules:
   attention  page gather, causal/window mask, masked softmax attention in fp64,
              log-sum-exp combine of split partials
   brute      pure-Python loops (math.exp / math.fsum) for tiny cases
+  cache_write  the paged KV-cache write: quantize new K/V and store them at their slots
 
 Parity pins: every function here is pinned in ``tests/test_oracle_*.py`` by a
 closed form, the torch ``float8_e4m3fn`` cast, brute force or an invariant.
 The pages print no worked numeric example, so no value from the pages pins
 the attention outputs directly.
 """
-from . import e4m3, attention, brute  # noqa: F401
+from . import e4m3, attention, brute, cache_write  # noqa: F401
 from .e4m3 import E4M3_TABLE, e4m3_decode, quantize_e4m3, dequantize_e4m3, descale_from_amax  # noqa: F401
 from .attention import (gather_pages, visible_mask, paged_attention, combine_splits,  # noqa: F401
                         split_attention, query_values)
+from .cache_write import slots_for_new_tokens  # noqa: F401

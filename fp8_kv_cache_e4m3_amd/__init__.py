@@ -6,7 +6,7 @@ library is missing, importing this package raises: there is no fallback path.
 
 The functions carry the C names (see include/fp8attn.h):
   fp8attn_quantize_q, fp8attn_prefill_varlen, fp8attn_decode_paged,
-  fp8attn_splitkv_combine, fp8attn_last_error, fp8attn_version
+  fp8attn_splitkv_combine, fp8attn_cache_write, fp8attn_last_error, fp8attn_version
 """
 from __future__ import annotations
 
@@ -78,6 +78,9 @@ _lib.fp8attn_decode_paged.argtypes = [ctypes.POINTER(AttnArgs), _i32, _vp, _sz, 
 _lib.fp8attn_decode_paged.restype = _i32
 _lib.fp8attn_splitkv_combine.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _vp, _i64, _i64, _vp, _vp]
 _lib.fp8attn_splitkv_combine.restype = _i32
+_lib.fp8attn_cache_write.argtypes = [_vp, _vp, _i64, _i32, _i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _i32,
+                                     _i64, _i64, _i64, _vp, _vp, _vp]
+_lib.fp8attn_cache_write.restype = _i32
 _lib.fp8attn_last_error.argtypes = []
 _lib.fp8attn_last_error.restype = ctypes.c_char_p
 _lib.fp8attn_version.argtypes = []
@@ -121,6 +124,25 @@ def _bytes(t):
     if t is not None and t.dtype == torch.float8_e4m3fn:
         return t.view(torch.uint8)
     return t
+
+
+def fp8attn_cache_write(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                        k_cache: torch.Tensor, v_cache: torch.Tensor, k_descale=None, v_descale=None,
+                        stream=None) -> None:
+    """Quantize bf16 k_new/v_new [T, Hkv, d] and store them at slot_mapping (int64 [T]) in the
+    E4M3 caches [pages, page_size, Hkv, d] (uint8 or float8_e4m3fn, d contiguous), in place."""
+    k_cache, v_cache = _bytes(k_cache), _bytes(v_cache)
+    assert k_new.dtype == torch.bfloat16 and v_new.dtype == torch.bfloat16 and k_new.shape == v_new.shape
+    assert k_new.stride(2) == 1 and v_new.stride(2) == 1 and k_cache.stride(3) == 1
+    assert k_cache.shape == v_cache.shape and k_cache.stride() == v_cache.stride()
+    assert slot_mapping.dtype == torch.int64 and slot_mapping.numel() == k_new.shape[0]
+    T, H, d = k_new.shape
+    st = _lib.fp8attn_cache_write(_ptr(k_new), _ptr(v_new), T, H, d, k_new.stride(0), k_new.stride(1),
+                                  v_new.stride(0), v_new.stride(1), _ptr(slot_mapping), _ptr(k_cache),
+                                  _ptr(v_cache), k_cache.shape[0], k_cache.shape[1], k_cache.stride(0),
+                                  k_cache.stride(1), k_cache.stride(2), _ptr(k_descale), _ptr(v_descale),
+                                  _stream(stream))
+    _check("fp8attn_cache_write", st)
 
 
 def fp8attn_quantize_q(q: torch.Tensor, q_descale=None, out=None, stream=None) -> torch.Tensor:

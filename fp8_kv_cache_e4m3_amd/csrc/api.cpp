@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -248,6 +249,64 @@ fp8attn_status fp8attn_quantize_q(const void* q_bf16, int64_t num_tokens, int32_
     return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: q_bf16 must be 16-byte and q_e4m3_out 8-byte aligned", fn);
   hipError_t e = fp8attn::launch_quantize_q(q_bf16, num_tokens, num_heads, head_dim, stride_tok, stride_head,
                                             q_descale, q_e4m3_out, stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
+fp8attn_status fp8attn_cache_write(const void* k_new, const void* v_new, int64_t num_tokens, int32_t num_kv_heads,
+                                   int32_t head_dim, int64_t k_stride_tok, int64_t k_stride_head, int64_t v_stride_tok,
+                                   int64_t v_stride_head, const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                   int64_t num_pages, int32_t page_size, int64_t kv_stride_page, int64_t kv_stride_tok,
+                                   int64_t kv_stride_head, const float* k_descale, const float* v_descale,
+                                   hipStream_t stream) {
+  const char* fn = "fp8attn_cache_write";
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_pages < 0 || page_size <= 0)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: num_tokens >= 0, num_pages >= 0, num_kv_heads > 0, head_dim > 0 and "
+                "page_size > 0 required", fn);
+  if (head_dim % 16 != 0)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: head_dim %d is not a multiple of 16 (k=e4m3 v=e4m3)", fn, head_dim);
+  const int64_t bstr[4] = {k_stride_tok, k_stride_head, v_stride_tok, v_stride_head};
+  for (int64_t x : bstr)
+    if (x < 0 || (x * 2) % 16 != 0)
+      return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: k_new/v_new strides must be non-negative multiples of 8 elements", fn);
+  if (kv_stride_page < 0 || kv_stride_tok < 0 || kv_stride_head < 0 || kv_stride_page % 16 != 0 ||
+      kv_stride_tok % 16 != 0 || kv_stride_head % 16 != 0)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: cache strides must be non-negative multiples of 16 bytes", fn);
+  const int64_t chunks = 2 * (int64_t)num_kv_heads * (head_dim / 16);
+  const int64_t bpt = (chunks + 255) / 256;
+  if (num_tokens * bpt > INT32_MAX)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: %lld tokens exceed one launch", fn, (long long)num_tokens);
+  if (num_pages > INT64_MAX / page_size)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: num_pages * page_size overflows", fn);
+  if (num_tokens == 0) return ok();
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: k_new, v_new, slot_mapping, k_cache and v_cache must be non-NULL", fn);
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8))
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: k_new, v_new and the caches must be 16-byte aligned, slot_mapping "
+                "8-byte aligned", fn);
+  fp8attn::CacheWriteParams p{};
+  p.k_new = static_cast<const __bf16*>(k_new);
+  p.v_new = static_cast<const __bf16*>(v_new);
+  p.k_stride_tok = k_stride_tok;
+  p.k_stride_head = k_stride_head;
+  p.v_stride_tok = v_stride_tok;
+  p.v_stride_head = v_stride_head;
+  p.slot_mapping = slot_mapping;
+  p.k_cache = static_cast<uint8_t*>(k_cache);
+  p.v_cache = static_cast<uint8_t*>(v_cache);
+  p.kv_stride_page = kv_stride_page;
+  p.kv_stride_tok = kv_stride_tok;
+  p.kv_stride_head = kv_stride_head;
+  p.num_tokens = num_tokens;
+  p.num_slots = num_pages * page_size;
+  p.page_size = page_size;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.blocks_per_token = (int32_t)bpt;
+  p.k_descale = k_descale;
+  p.v_descale = v_descale;
+  hipError_t e = fp8attn::launch_cache_write(p, stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   return ok();
 }

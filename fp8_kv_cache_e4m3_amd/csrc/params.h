@@ -45,6 +45,25 @@ constexpr int kQBf16 = 0;       // bf16 values, BF16 MFMA with K/V dequantized
 constexpr int kQE4M3 = 1;       // E4M3 codes, FP8 MFMA
 constexpr int kQBf16E4M3 = 2;   // bf16 values quantized to E4M3 on load, FP8 MFMA
 
+// KV-cache write (fp8attn_cache_write)
+struct CacheWriteParams {
+  const __bf16* k_new;
+  const __bf16* v_new;
+  int64_t k_stride_tok, k_stride_head, v_stride_tok, v_stride_head;   // elements
+  const int64_t* slot_mapping;
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  int64_t kv_stride_page, kv_stride_tok, kv_stride_head;              // bytes
+  int64_t num_tokens;
+  int64_t num_slots;            // num_pages * page_size
+  int32_t page_size;
+  int32_t num_kv_heads, head_dim;
+  int32_t blocks_per_token;     // ceil(2 * num_kv_heads * head_dim / 16 / 256)
+  const float* k_descale;       // NULL -> 1
+  const float* v_descale;
+};
+hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream);
+
 hipError_t launch_quantize_q(const void* q, int64_t ntok, int32_t nheads, int32_t d,
                              int64_t stride_tok, int64_t stride_head, const float* q_descale,
                              void* out, hipStream_t stream);

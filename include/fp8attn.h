@@ -168,6 +168,34 @@ fp8attn_status fp8attn_splitkv_combine(const float* partial_o, const float* part
                                        int32_t head_dim, void* out_bf16, int64_t out_stride_tok,
                                        int64_t out_stride_head, float* lse_out, hipStream_t stream);
 
+/*
+ * Paged KV-cache write ([60372] Details, "Why FP8 is slower than BF16": the KV-cache write
+ * kernels reshape the new keys and values and store them into the paged cache, converting them
+ * for an FP8 cache).  For every token t whose slot s = slot_mapping[t] lies in
+ * [0, num_pages * page_size):
+ *   k_cache[s / page_size, s % page_size, h, :] = E4M3_RNE_SAT(float32(k_new[t, h, :]) / float32(*k_descale))
+ *   v_cache[...same...]                         = E4M3_RNE_SAT(float32(v_new[t, h, :]) / float32(*v_descale))
+ * with the rounding of fp8attn_quantize_q.  Other tokens (padding carries -1) write nothing, so a
+ * slot out of range is never an out-of-bounds store.  Slots must be distinct: with a repeated
+ * slot the entry ends up holding one of the tokens, which one is unspecified.
+ *   k_new, v_new       : bf16 [num_tokens, num_kv_heads, head_dim], element strides per tensor
+ *                        (head_dim contiguous), 16-byte aligned
+ *   slot_mapping       : device int64 [num_tokens]
+ *   k_cache, v_cache   : E4M3 bytes [num_pages, page_size, num_kv_heads, head_dim] with byte
+ *                        strides kv_stride_page / kv_stride_tok / kv_stride_head (the layout of
+ *                        fp8attn_attn_args), 16-byte aligned
+ *   k_descale, v_descale: device fp32 scalars, or NULL for 1.0
+ * head_dim must be a multiple of 16, page_size >= 1, and every stride a multiple of 16 bytes.
+ * num_tokens == 0 is a no-op.  Nothing is allocated; the work is enqueued on the stream.
+ */
+fp8attn_status fp8attn_cache_write(const void* k_new, const void* v_new, int64_t num_tokens,
+                                   int32_t num_kv_heads, int32_t head_dim, int64_t k_stride_tok,
+                                   int64_t k_stride_head, int64_t v_stride_tok, int64_t v_stride_head,
+                                   const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                   int64_t num_pages, int32_t page_size, int64_t kv_stride_page,
+                                   int64_t kv_stride_tok, int64_t kv_stride_head,
+                                   const float* k_descale, const float* v_descale, hipStream_t stream);
+
 /* Text of the last error on the calling thread ("" after a successful call).  Messages for
  * unsupported combinations name the q/k/v dtypes and head sizes ([60372] review thread). */
 const char* fp8attn_last_error(void);

@@ -164,3 +164,23 @@ def test_decode_workspace_query_needs_no_gpu_reads():
     buf = torch.zeros(64, dtype=torch.uint8)
     st = fa.LIB.fp8attn_decode_paged(ctypes.byref(a), 4, buf.data_ptr(), 64, None, None, None)
     assert st == fa.ERR_WORKSPACE and "workspace" in fa.fp8attn_last_error()
+
+
+def test_cache_write_rejections():
+    L = fa.LIB
+    args = lambda **kw: {**dict(k=None, v=None, T=4, H=2, d=32, kst=64, ksh=32, vst=64, vsh=32, slots=None,
+                                kc=None, vc=None, pages=3, ps=64, sp=64 * 64, stt=64, sth=32, kd=None, vd=None), **kw}
+    def call(a):
+        return L.fp8attn_cache_write(a["k"], a["v"], a["T"], a["H"], a["d"], a["kst"], a["ksh"], a["vst"], a["vsh"],
+                                     a["slots"], a["kc"], a["vc"], a["pages"], a["ps"], a["sp"], a["stt"], a["sth"],
+                                     a["kd"], a["vd"], None)
+    assert call(args(d=24)) == fa.ERR_UNSUPPORTED and "multiple of 16" in fa.fp8attn_last_error()
+    assert call(args(H=0)) == fa.ERR_INVALID_ARG
+    assert call(args(ps=0)) == fa.ERR_INVALID_ARG
+    assert call(args(T=-1)) == fa.ERR_INVALID_ARG
+    assert call(args(kst=60)) == fa.ERR_UNSUPPORTED and "strides" in fa.fp8attn_last_error()
+    assert call(args(stt=40)) == fa.ERR_UNSUPPORTED and "cache strides" in fa.fp8attn_last_error()
+    assert call(args()) == fa.ERR_INVALID_ARG and "non-NULL" in fa.fp8attn_last_error()
+    assert call(args(T=0)) == fa.OK
+    assert call(args(k=0x1008, v=0x2000, slots=0x3000, kc=0x4000, vc=0x5000)) == fa.ERR_UNSUPPORTED
+    assert "aligned" in fa.fp8attn_last_error()

@@ -183,6 +183,48 @@ def time_workload(make, entry, nsets, steps, warmup, label, fused=True):
     return out
 
 
+def time_cache_write(make, steps, label):
+    """The KV-cache write of a workload's new tokens (bf16 K/V for every new token and kv head,
+    stored at the tokens' slots in the workload's pools), timed with events around `steps`
+    back-to-back calls that alternate between two input sets.  Algorithmic bytes: bf16 K and V
+    read, E4M3 codes written, the slot ids read."""
+    import numpy as np
+    import torch
+    import fp8_kv_cache_e4m3_amd as fa
+    sets = []
+    for seed in range(2):
+        w = make(seed)
+        T, H, d = w.total_q, w.num_kv_heads, w.head_dim
+        ps = w.k_pool.shape[1]
+        bt = w.block_table.cpu().numpy()
+        slots = []
+        for b, (L, ql) in enumerate(zip(w.seqlens_k_host, w.q_lens_host)):
+            j = np.arange(L - ql, L)
+            slots.append(bt[b][j // ps].astype(np.int64) * ps + j % ps)
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        sets.append((torch.randn((T, H, d), generator=g, device="cuda").to(torch.bfloat16),
+                     torch.randn((T, H, d), generator=g, device="cuda").to(torch.bfloat16),
+                     torch.from_numpy(np.concatenate(slots)).cuda(), w.k_pool, w.v_pool, w.k_descale, w.v_descale))
+    w = sets[0]
+    T, H, d = w[0].shape
+    nbytes = 2 * T * H * d * 2 + 2 * T * H * d + 8 * T
+    for i in range(4):
+        fa.fp8attn_cache_write(*sets[i % 2])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(steps):
+        fa.fp8attn_cache_write(*sets[i % 2])
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    log(f"[bench] {label}: {T} tokens x {H} kv heads x d{d}: {ms:.4f} ms")
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"KV-cache write, {T} new tokens x {H} kv heads x d{d}", "ms_per_call": round(ms, 4),
+            "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}
+
+
 def cpu_baseline(budget_s=15.0):
     """The CPU oracle, as is, on a bounded sample of the sliding-window decode workload: whole
     sequences (all 32 q heads) until the time budget is spent.  Rate = the same algorithmic bytes
@@ -328,6 +370,9 @@ def main():
                 peak = FP8_PEAK_TFLOPS if ww.q_dtype == "e4m3" else BF16_PEAK_TFLOPS
                 e["mfma_frac"] = round(e["TFLOPs"] / peak, 4)
             extra[name] = e
+        for name, make in [("kv_write_swa_prefill", lambda s: wl.swa_prefill(device="cuda", seed=400 + s)),
+                           ("kv_write_swa_decode", lambda s: wl.swa_decode(device="cuda", seed=100 + s))]:
+            extra[name] = time_cache_write(make, max(5, args.steps // 5), name)
 
     cpu = None
     if not args.no_cpu:

@@ -221,7 +221,7 @@ DecodePlan plan_decode(const fp8attn_attn_args* a, int32_t requested) {
     const size_t rows = (size_t)a->total_q * a->num_q_heads;
     pl.ws_bytes = round_up(S * rows * a->head_dim * sizeof(float)) + round_up(S * rows * sizeof(float));
   }
-  pl.grid = items * S;
+  pl.grid = items * S;   // the caller rejects grids of 2^31 blocks or more
   return pl;
 }
 

@@ -125,17 +125,29 @@ __global__ void __launch_bounds__(256)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
 
-  // ---- work item -------------------------------------------------------------------------
-  int64_t id = xcd_remap(blockIdx.x, gridDim.x);
-  const int rt = (int)(id % p.row_groups); id /= p.row_groups;
-  const int b = (int)(id % p.batch); id /= p.batch;
-  const int s = (int)(id % p.num_splits); id /= p.num_splits;
-  const int h = (int)id;
+  // ---- work item (32-bit index arithmetic: the host keeps the grid below 2^31) ----------
+  uint32_t id = xcd_remap32(blockIdx.x, gridDim.x);
+  const uint32_t n_rt = (uint32_t)p.row_groups, n_b = (uint32_t)p.batch, n_s = (uint32_t)p.num_splits;
+  const int rt = (int)(id % n_rt); id /= n_rt;
+  const int b = (int)(id % n_b); id /= n_b;
+  const int s = (int)(id % n_s);
+  const int h = (int)(id / n_s);
   const int G = p.group;
 
-  const int t0 = p.cu_seqlens_q[b];
-  const int ql = p.cu_seqlens_q[b + 1] - t0;
-  const int L = p.seqlens_k[b];
+  // Every per-item scalar of the prologue is requested here, before any branch, so that the
+  // loads share one round trip.  A NULL descale reads a valid stand-in address (the sequence's
+  // length) and is replaced by 1 below.
+  const int64_t dsi = (int64_t)b * p.ds_stride_b + (int64_t)h * p.ds_stride_h;
+  const int t0 = load_uniform(p.cu_seqlens_q, b);
+  const int t1 = load_uniform(p.cu_seqlens_q, b + 1);
+  const int L = load_uniform(p.seqlens_k, b);
+  const float* stand_in = reinterpret_cast<const float*>(p.seqlens_k);
+  const float kd_raw = load_uniform(p.k_descale ? p.k_descale : stand_in, p.k_descale ? dsi : 0);
+  const float vd_raw = load_uniform(p.v_descale ? p.v_descale : stand_in, p.v_descale ? dsi : 0);
+  const float qd_raw = load_uniform(p.q_descale ? p.q_descale : stand_in, 0);
+  // (the compiler would otherwise sink each load to its first use, behind the branches below)
+  asm volatile("" ::"s"(t0), "s"(t1), "s"(L), "s"(kd_raw), "s"(vd_raw), "s"(qd_raw));
+  const int ql = t1 - t0;
   const int nrows = ql * G;
   const int row0 = rt * 16;
   if (row0 >= nrows) return;
@@ -164,10 +176,9 @@ __global__ void __launch_bounds__(256)
     return;
   }
 
-  const int64_t dsi = (int64_t)b * p.ds_stride_b + (int64_t)h * p.ds_stride_h;
-  const float kd = p.k_descale ? load_uniform(p.k_descale, dsi) : 1.0f;
-  const float vd = p.v_descale ? load_uniform(p.v_descale, dsi) : 1.0f;
-  const float qd = QFP8 && p.q_descale ? load_uniform(p.q_descale, 0) : 1.0f;
+  const float kd = p.k_descale ? kd_raw : 1.0f;
+  const float vd = p.v_descale ? vd_raw : 1.0f;
+  const float qd = QFP8 && p.q_descale ? qd_raw : 1.0f;
   const float cscale = p.scale_log2 * kd * qd;
 
   // Page ids of the split's keys: lane i holds the id of page pg_base + i (clamped to the split's

@@ -28,6 +28,9 @@ constexpr float kNegInf = -__builtin_inff();
 __device__ __forceinline__ float load_uniform(const float* p, int64_t i) {
   return ((const __attribute__((address_space(4))) float*)p)[i];
 }
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
 
 // ---------------------------------------------------------------------------------------------
 // Direct-to-LDS loads, issued from inline assembly on purpose: the compiler then does not track
@@ -185,6 +188,12 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // XCD-aware remap: the dispatcher sends block i to XCD i % 8.  Give each XCD a contiguous
 // range of logical ids so that neighbouring work items (which share K/V pages) share an L2.
 // ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t xcd_remap32(uint32_t bid, uint32_t n) {
+  constexpr uint32_t kXcd = 8;
+  const uint32_t per = n / kXcd, rem = n % kXcd;
+  const uint32_t x = bid % kXcd, k = bid / kXcd;
+  return x * per + (x < rem ? x : rem) + k;
+}
 __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t n) {
   constexpr int64_t kXcd = 8;
   const int64_t per = n / kXcd, rem = n % kXcd;

@@ -246,10 +246,19 @@ __global__ void __launch_bounds__(256)
   uoff.k = (uint32_t)(col * sT) + 16u * (uint32_t)grp;
 #pragma unroll
   for (int i = 0; i < 4; ++i) uoff.v[i] = (uint32_t)((4 * grp + i) * sT) + (uint32_t)(col * S::CW);
+  // Loads past the split's last unit keep the number of loads per trip fixed, so that the
+  // compiler waits for exactly the oldest unit.  They read the last unit's first 16 bytes in every
+  // lane: one cache line, which costs next to nothing and lands quickly at the end of the stream.
+  const int ulast = su1 - 1;
   auto issue = [&](UnitRegs<D>& ur, int u) __attribute__((always_inline)) {
-    const int j0 = u * 16;
-    const int64_t unit = page_of(u) * sP + (int64_t)(j0 % ps) * sT;
-    load_unit<D, T::NT>(ur, kbase + unit, vbase + unit, uoff);
+    const bool trailing = u > ulast;
+    const int uc = trailing ? ulast : u;
+    const int64_t unit = page_of(uc) * sP + (int64_t)((uc * 16) % ps) * sT;
+    UnitOffsets o = uoff;
+    o.k = trailing ? 0u : o.k;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.v[i] = trailing ? 0u : o.v[i];
+    load_unit<D, T::NT>(ur, kbase + unit, vbase + unit, o);
   };
 
   // S^T tile of a unit: rows = its 16 keys, columns = the 16 query rows
@@ -331,15 +340,13 @@ __global__ void __launch_bounds__(256)
 
   // ---- main loop: this wave takes units su0+wave, su0+wave+4, ... --------------------------
   const int u0 = su0 + wave;
-  const int ulast = su1 - 1;
   {
     // A ring of NBUF register buffers: NBUF - 1 units stay in flight while one is computed.
-    // Every trip issues the same loads (indices past the end are clamped to the split's last
-    // unit, an in-bounds re-read that hits L2), so the compiler can wait for exactly the oldest
-    // unit instead of draining every outstanding load.
+    // Every trip issues the same loads (see issue), so the compiler can wait for exactly the
+    // oldest unit instead of draining every outstanding load.
     UnitRegs<D> buf[NBUF];
 #pragma unroll
-    for (int k = 0; k < NBUF; ++k) issue(buf[k], min(u0 + 4 * k, ulast));
+    for (int k = 0; k < NBUF; ++k) issue(buf[k], u0 + 4 * k);
     if constexpr (QM == kQBf16E4M3) {
       // quantize bf16 Q with the arithmetic of the stand-alone quantize call (identical codes)
       const double rcp = 1.0 / (double)qd;
@@ -354,7 +361,7 @@ __global__ void __launch_bounds__(256)
       for (int k = 0; k < NBUF; ++k) {
         const int uk = u + 4 * k;
         if (uk < su1) compute(buf[k], uk);
-        issue(buf[k], min(uk + 4 * NBUF, ulast));
+        issue(buf[k], uk + 4 * NBUF);
       }
     }
   }

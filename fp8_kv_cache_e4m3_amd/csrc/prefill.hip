@@ -111,13 +111,17 @@ __device__ __forceinline__ int load_instruction(int wave, int k) {
   const int ins = wave + S::NW * k;
   return ins < S::LOADS ? ins : ins - S::NW;
 }
+// idle: a load past the block's last tile, which only keeps the number of loads per interval
+// fixed.  Its lanes all read the tile's first 16 bytes (one cache line) into the free stage.
 template <int D>
-__device__ __forceinline__ void tile_load_step(const TileLoad& tl, const uint32_t* loff, int wave, int k) {
+__device__ __forceinline__ void tile_load_step(const TileLoad& tl, const uint32_t* loff, int wave, int k,
+                                               bool idle) {
   using S = PrefillShape<D>;
   const int ins = load_instruction<D>(wave, k);
   const int which = ins / S::SLOTS;
   const int blk = ins % S::SLOTS;
-  lds_dma16(which ? tl.v_src : tl.k_src, loff[k], tl.lds_stage + (uint32_t)(which * S::TILE + blk * 1024));
+  lds_dma16(which ? tl.v_src : tl.k_src, idle ? 0u : loff[k],
+            tl.lds_stage + (uint32_t)(which * S::TILE + blk * 1024));
 }
 
 // The MFMA work of one wave between two barriers: O^T += V^T * P^T for one tile (PV) and then
@@ -186,14 +190,26 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
 
   // ---- work item: (sequence, kv head) outer, q block descending (heaviest first) -----------
   // the block grid covers q blocks [0, qb_end) of every (sequence, kv head)
-  int64_t id = xcd_remap(blockIdx.x, gridDim.x);
-  const int qb = qb_end - 1 - (int)(id % qb_end); id /= qb_end;
-  const int h = (int)(id % p.hkv); id /= p.hkv;
-  const int b = (int)id;
+  // (32-bit index arithmetic: the host keeps the grid below 2^31)
+  uint32_t id = xcd_remap32(blockIdx.x, gridDim.x);
+  const int qb = qb_end - 1 - (int)(id % (uint32_t)qb_end); id /= (uint32_t)qb_end;
+  const int h = (int)(id % (uint32_t)p.hkv);
+  const int b = (int)(id / (uint32_t)p.hkv);
   const int G = p.group;
-  const int t0 = p.cu_seqlens_q[b];
-  const int ql = p.cu_seqlens_q[b + 1] - t0;
-  const int L = p.seqlens_k[b];
+  // Every per-item scalar of the prologue is requested here, before any branch, so that the
+  // loads share one round trip.  A NULL descale reads a valid stand-in address (the sequence's
+  // length) and is replaced by 1 below.
+  const int64_t dsi = (int64_t)b * p.ds_stride_b + (int64_t)h * p.ds_stride_h;
+  const int t0 = load_uniform(p.cu_seqlens_q, b);
+  const int t1 = load_uniform(p.cu_seqlens_q, b + 1);
+  const int L = load_uniform(p.seqlens_k, b);
+  const float* stand_in = reinterpret_cast<const float*>(p.seqlens_k);
+  const float kd_raw = load_uniform(p.k_descale ? p.k_descale : stand_in, p.k_descale ? dsi : 0);
+  const float vd_raw = load_uniform(p.v_descale ? p.v_descale : stand_in, p.v_descale ? dsi : 0);
+  const float qd_raw = load_uniform(p.q_descale ? p.q_descale : stand_in, 0);
+  // (the compiler would otherwise sink each load to its first use, behind the branches below)
+  asm volatile("" ::"s"(t0), "s"(t1), "s"(L), "s"(kd_raw), "s"(vd_raw), "s"(qd_raw));
+  const int ql = t1 - t0;
   const int nrows = ql * G;
   const int r0 = qb * S::BM;
   if (r0 >= nrows) return;
@@ -221,9 +237,9 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   const int min_keys = W >= 1 ? min(pf + 1, W) : pf + 1;
   if ((min_keys < kSplitPKeys) != SPLIT) return;
 
-  const float kd = p.k_descale ? p.k_descale[b * p.ds_stride_b + h * p.ds_stride_h] : 1.0f;
-  const float vd = p.v_descale ? p.v_descale[b * p.ds_stride_b + h * p.ds_stride_h] : 1.0f;
-  const float qd = p.q_descale ? p.q_descale[0] : 1.0f;
+  const float kd = p.k_descale ? kd_raw : 1.0f;
+  const float vd = p.v_descale ? vd_raw : 1.0f;
+  const float qd = p.q_descale ? qd_raw : 1.0f;
   const float cs = p.scale_log2 * kd * qd;
 
   // ---- Q^T operand: lane (row lr, half lg) holds Q[row][64c + 32lg .. +32] per k-step c -------
@@ -283,12 +299,12 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
     return bt[ps == S::BK ? kt : (kt * S::BK) / ps];
   };
   // issue this wave's loads of tile kt (page id page) into the stage at byte offset so
-  auto issue = [&](int so, int kt, int page) __attribute__((always_inline)) {
+  auto issue = [&](int so, int kt, int page, bool idle = false) __attribute__((always_inline)) {
     const int slot0 = ps == S::BK ? 0 : kt * S::BK - ((kt * S::BK) / ps) * ps;
     const int64_t tile_off = (int64_t)page * sP + (int64_t)slot0 * sT;
     const TileLoad tl{kbase + tile_off, vbase + tile_off, lds_base + (uint32_t)so};
 #pragma unroll
-    for (int k = 0; k < S::MAXI; ++k) tile_load_step<D>(tl, loff, wave, k);
+    for (int k = 0; k < S::MAXI; ++k) tile_load_step<D>(tl, loff, wave, k, idle);
   };
 
   // Row assignments.  MFMA row m of a 32-key half tile holds key kperm(m), which swaps bits 2
@@ -397,8 +413,8 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   // load issue is staggered.  Only tiles t and t+1 are read in interval t; tile t+2 is landing
   // (it is needed after barrier t+1) and tile t+3 goes into the stage tile t-1 has left, so a
   // tile's loads have more than an interval to land.  Before each barrier a wave waits for all
-  // its loads but the ones of the interval that ends there.  Loads past the last tile fetch the
-  // last tile again into the free stage, which keeps the number of loads the same every interval.
+  // its loads but the ones of the interval that ends there.  Loads past the last tile read one
+  // cache line into the free stage, which keeps the number of loads the same every interval.
   const bool grpB = wave >= S::NW / 2;
   // Before a barrier: the loads older than this interval's have landed.  Also a scheduling fence:
   // the compiler may not move the softmax or MFMA work of one half period across the barrier into
@@ -413,12 +429,12 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   // page id of the tile interval I loads (tile min(I + 3, kt1)), read one interval ahead
   int page_ahead = page_id(min(kt0 + 2, kt1));
   auto interval_loads = [&](int I) __attribute__((always_inline)) {
-    issue(stage_of(I + 3), min(I + 3, kt1), page_ahead);
+    issue(stage_of(I + 3), min(I + 3, kt1), page_ahead, I + 3 > kt1);
     page_ahead = page_id(min(I + 4, kt1));
   };
 
   issue(stage_of(kt0), kt0, page_id(kt0));
-  issue(stage_of(kt0 + 1), min(kt0 + 1, kt1), page_id(min(kt0 + 1, kt1)));
+  issue(stage_of(kt0 + 1), min(kt0 + 1, kt1), page_id(min(kt0 + 1, kt1)), kt0 + 1 > kt1);
   if constexpr (QBF16) {
     // The same 32 d values per k-step as the E4M3 codes, read as bf16 and quantized here, with
     // the arithmetic of the stand-alone quantize call (identical codes).  Every load is issued

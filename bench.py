@@ -34,6 +34,8 @@ BF16_PEAK_TFLOPS = 2500.0      # dense BF16 MFMA
 # sources each measured kernel is built from: a recorded traffic figure is used only while they
 # are unchanged
 KERNEL_SOURCES = {
+    "cache_write": ["fp8_kv_cache_e4m3_amd/csrc/cache_write.hip", "fp8_kv_cache_e4m3_amd/csrc/device.h",
+                    "fp8_kv_cache_e4m3_amd/csrc/params.h"],
     "decode": ["fp8_kv_cache_e4m3_amd/csrc/decode.hip", "fp8_kv_cache_e4m3_amd/csrc/device.h",
                "fp8_kv_cache_e4m3_amd/csrc/params.h"],
     "prefill": ["fp8_kv_cache_e4m3_amd/csrc/prefill.hip", "fp8_kv_cache_e4m3_amd/csrc/device.h",
@@ -222,7 +224,8 @@ def time_cache_write(make, steps, label):
     log(f"[bench] {label}: {T} tokens x {H} kv heads x d{d}: {ms:.4f} ms")
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": f"KV-cache write, {T} new tokens x {H} kv heads x d{d}", "ms_per_call": round(ms, 4),
-            "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}
+            "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+            "traffic": load_traffic(label) if label == "kv_write_swa_prefill" else None}
 
 
 def cpu_baseline(budget_s=15.0):
@@ -298,7 +301,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="only the main workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--profile-pass", default=None,
-                    choices=["swa_decode", "full_decode", "spec_verify", "swa_prefill"],
+                    choices=["swa_decode", "full_decode", "spec_verify", "swa_prefill", "kv_write_swa_prefill"],
                     help="short run for rocprofv3 counter passes: one workload plus a 1 GiB device copy")
     ap.add_argument("--separate-quantize", action="store_true",
                     help="quantize Q with its own call before attention (two launches per step) instead of "
@@ -332,6 +335,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
+        if args.profile_pass == "kv_write_swa_prefill":
+            time_cache_write(lambda s: wl.swa_prefill(device="cuda", seed=400 + s), args.steps, "kv_write (profile pass)")
+            return
         make, entry = makers[args.profile_pass]
         time_workload(make, entry, 2, args.steps, args.warmup, f"{args.profile_pass} (profile pass)", fused)
         return

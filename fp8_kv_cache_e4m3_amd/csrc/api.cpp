@@ -61,10 +61,13 @@ int cu_count() {
 }
 
 // Supported (q dtype, head dim) pairs: native FP8 at head dim 256 (vLLM PR #63139, Overview) and
-// BF16 Q at head dim 512 (vLLM PR #60372, Overview), plus head dim 64 for both as a small case.
+// BF16 Q at head dim 512 (vLLM PR #60372, Overview), plus head dims 64, 128 and 192 for both
+// (vLLM PR #63139, Overview: the FA4 native FP8 forward also covers 64/96/128/192; 96 is not a
+// multiple of the 64-wide FP8 MFMA k-step and is not built).
 bool supported_combo(int32_t q_dtype, int32_t d) {
-  if (q_dtype == FP8ATTN_E4M3 || q_dtype == FP8ATTN_BF16_TO_E4M3) return d == 64 || d == 256;
-  if (q_dtype == FP8ATTN_BF16) return d == 64 || d == 512;
+  const bool small = d == 64 || d == 128 || d == 192;
+  if (q_dtype == FP8ATTN_E4M3 || q_dtype == FP8ATTN_BF16_TO_E4M3) return small || d == 256;
+  if (q_dtype == FP8ATTN_BF16) return small || d == 512;
   return false;
 }
 
@@ -83,7 +86,8 @@ fp8attn_status validate_attn(const char* fn, const fp8attn_attn_args* a, bool de
   if (!supported_combo(a->q_dtype, a->head_dim))
     return fail(FP8ATTN_ERR_UNSUPPORTED,
                 "%s: unsupported combination q=%s k=e4m3 v=e4m3 head_size=%d head_size_v=%d "
-                "(supported: q=e4m3 or bf16->e4m3 with head_size 64 or 256; q=bf16 with head_size 64 or 512; "
+                "(supported: q=e4m3 or bf16->e4m3 with head_size 64, 128, 192 or 256; q=bf16 with head_size 64, 128, "
+                "192 or 512; "
                 "k/v always e4m3 with head_size_v == head_size)",
                 fn, dtype_name(a->q_dtype), a->head_dim, a->head_dim);
   if (a->causal != 1)
@@ -385,8 +389,8 @@ fp8attn_status fp8attn_splitkv_combine(const float* partial_o, const float* part
   const char* fn = "fp8attn_splitkv_combine";
   if (num_splits <= 0 || total_q < 0 || num_q_heads <= 0)
     return fail(FP8ATTN_ERR_INVALID_ARG, "%s: num_splits > 0, total_q >= 0 and num_q_heads > 0 required", fn);
-  if (head_dim != 64 && head_dim != 256 && head_dim != 512)
-    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 256, 512}", fn, head_dim);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 192 && head_dim != 256 && head_dim != 512)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128, 192, 256, 512}", fn, head_dim);
   if (out_stride_tok < 0 || out_stride_head < 0)
     return fail(FP8ATTN_ERR_INVALID_ARG, "%s: output strides must be >= 0", fn);
   if (total_q == 0) return ok();

@@ -66,6 +66,12 @@ hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t S,
   else if (d == 256)
     hipLaunchKernelGGL(combine_kernel<256>, g, blk, 0, stream, part_o, part_lse, S, rows, hq, o,
                        out_stride_tok, out_stride_head, lse_out);
+  else if (d == 192)
+    hipLaunchKernelGGL(combine_kernel<192>, g, blk, 0, stream, part_o, part_lse, S, rows, hq, o,
+                       out_stride_tok, out_stride_head, lse_out);
+  else if (d == 128)
+    hipLaunchKernelGGL(combine_kernel<128>, g, blk, 0, stream, part_o, part_lse, S, rows, hq, o,
+                       out_stride_tok, out_stride_head, lse_out);
   else
     hipLaunchKernelGGL(combine_kernel<64>, g, blk, 0, stream, part_o, part_lse, S, rows, hq, o,
                        out_stride_tok, out_stride_head, lse_out);

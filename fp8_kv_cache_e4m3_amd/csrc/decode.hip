@@ -40,7 +40,7 @@ struct DecodeShape {
   static constexpr int VBLK = D / (16 * CW);          // V column blocks
   static constexpr int NT = D / 16;                   // O^T tiles (16 d-rows each)
   static constexpr int RS = D + 4;                    // LDS row stride (floats), padded
-  static_assert(D == 64 || D == 256 || D == 512, "head dim");
+  static_assert(D == 64 || D == 128 || D == 192 || D == 256 || D == 512, "head dim");
 };
 
 template <int D>
@@ -82,8 +82,14 @@ __device__ __forceinline__ void load_unit(UnitRegs<D>& ur, const uint8_t* __rest
         ur.v[i][blk][1] = w[1];
         ur.v[i][blk][2] = w[2];
         ur.v[i][blk][3] = w[3];
-      } else {
-        ur.v[i][blk][0] = stream_load<NT>(reinterpret_cast<const uint32_t*>(vp));
+      } else if constexpr (S::CW == 8) {
+        const u32x2_t w = stream_load<NT>(reinterpret_cast<const u32x2_t*>(vp));
+        ur.v[i][blk][0] = w[0];
+        ur.v[i][blk][1] = w[1];
+      } else {   // 4 or 12 bytes: dword loads
+#pragma unroll
+        for (int x = 0; x < S::CW / 4; ++x)
+          ur.v[i][blk][x] = stream_load<NT>(reinterpret_cast<const uint32_t*>(vp + 4 * x));
       }
     }
   }
@@ -439,20 +445,27 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+template <int QM>
+static void launch_decode_dims(const AttnParams& p, int head_dim, dim3 g, hipStream_t stream) {
+  const dim3 blk(256);
+  switch (head_dim) {
+    case 64: hipLaunchKernelGGL((decode_kernel<QM, 64>), g, blk, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((decode_kernel<QM, 128>), g, blk, 0, stream, p); break;
+    case 192: hipLaunchKernelGGL((decode_kernel<QM, 192>), g, blk, 0, stream, p); break;
+    default:
+      // the last head dim of each variant: 256 (FP8 Q) or 512 (BF16 Q)
+      if constexpr (QM == kQBf16) hipLaunchKernelGGL((decode_kernel<QM, 512>), g, blk, 0, stream, p);
+      else hipLaunchKernelGGL((decode_kernel<QM, 256>), g, blk, 0, stream, p);
+  }
+}
+
 hipError_t launch_decode(const AttnParams& p, int q_mode, int head_dim, int64_t grid,
                          hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  const dim3 g((unsigned)grid), blk(256);
-  if (q_mode == kQE4M3) {
-    if (head_dim == 256) hipLaunchKernelGGL((decode_kernel<kQE4M3, 256>), g, blk, 0, stream, p);
-    else hipLaunchKernelGGL((decode_kernel<kQE4M3, 64>), g, blk, 0, stream, p);
-  } else if (q_mode == kQBf16E4M3) {
-    if (head_dim == 256) hipLaunchKernelGGL((decode_kernel<kQBf16E4M3, 256>), g, blk, 0, stream, p);
-    else hipLaunchKernelGGL((decode_kernel<kQBf16E4M3, 64>), g, blk, 0, stream, p);
-  } else {
-    if (head_dim == 512) hipLaunchKernelGGL((decode_kernel<kQBf16, 512>), g, blk, 0, stream, p);
-    else hipLaunchKernelGGL((decode_kernel<kQBf16, 64>), g, blk, 0, stream, p);
-  }
+  const dim3 g((unsigned)grid);
+  if (q_mode == kQE4M3) launch_decode_dims<kQE4M3>(p, head_dim, g, stream);
+  else if (q_mode == kQBf16E4M3) launch_decode_dims<kQBf16E4M3>(p, head_dim, g, stream);
+  else launch_decode_dims<kQBf16>(p, head_dim, g, stream);
   return hipGetLastError();
 }
 

@@ -92,7 +92,7 @@ struct PrefillShape {
   static constexpr int LOADS = 2 * SLOTS; // wave-wide 1 KiB load instructions per K+V tile
   static constexpr int MAXI = (LOADS + NW - 1) / NW;  // load instructions per wave per tile
   static_assert(MAXI <= NDT + 2 * KSTEP, "loads are issued one per MFMA");
-  static_assert(D == 64 || D == 256, "head dim");
+  static_assert(D == 64 || D == 128 || D == 192 || D == 256, "head dim");
 };
 
 // Direct-to-LDS loads of one K and one V tile: D/16 + 1 16-byte slots per key row (the pad slot
@@ -531,6 +531,12 @@ hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, bool q_bf16, hi
   if (head_dim == 256) {
     if (q_bf16) launch_prefill_pair<256, true>(p, grid, nqb, grid_split, nqb_split, stream);
     else launch_prefill_pair<256, false>(p, grid, nqb, grid_split, nqb_split, stream);
+  } else if (head_dim == 192) {
+    if (q_bf16) launch_prefill_pair<192, true>(p, grid, nqb, grid_split, nqb_split, stream);
+    else launch_prefill_pair<192, false>(p, grid, nqb, grid_split, nqb_split, stream);
+  } else if (head_dim == 128) {
+    if (q_bf16) launch_prefill_pair<128, true>(p, grid, nqb, grid_split, nqb_split, stream);
+    else launch_prefill_pair<128, false>(p, grid, nqb, grid_split, nqb_split, stream);
   } else {
     if (q_bf16) launch_prefill_pair<64, true>(p, grid, nqb, grid_split, nqb_split, stream);
     else launch_prefill_pair<64, false>(p, grid, nqb, grid_split, nqb_split, stream);

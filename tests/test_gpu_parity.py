@@ -190,7 +190,8 @@ def test_combine_entry_point():
 # ------------------------------------------------------------------------------------------
 # gather: bit-exact (one-hot logits), page permutation invariance, determinism
 # ------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("q_dtype,d", [("bf16", 512), ("e4m3", 256), ("bf16", 64), ("e4m3", 64)])
+@pytest.mark.parametrize("q_dtype,d", [("bf16", 512), ("e4m3", 256), ("bf16", 64), ("e4m3", 64),
+                                       ("e4m3", 192), ("bf16", 128)])
 def test_one_hot_gather_bit_exact(q_dtype, d):
     """Q equal to one key's row with a huge softmax scale: every other weight is exactly 0 in
     fp32, so O must equal that key's dequantized V row bit for bit (v_descale a power of two)."""
@@ -250,6 +251,32 @@ def test_edge_cases(q_dtype, d, hq, hkv, window, seqlens, qlens, entry):
     if codes is not None:
         assert np.array_equal(codes, codes_ref)
     compare(o, o_ref, l, l_ref, label=f"edge {entry} S={splits}")
+
+
+# ------------------------------------------------------------------------------------------
+# head dims 128 and 192, both variants, both entry points; the in-kernel Q quantization gives
+# the two-call path's outputs bit for bit
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("d", [128, 192])
+@pytest.mark.parametrize("q_dtype,entry,splits", [
+    ("e4m3", "decode", 0), ("e4m3", "decode", 3), ("e4m3", "prefill", 0),
+    ("bf16", "decode", 0), ("bf16", "decode", 2), ("bf16", "prefill", 0),
+])
+def test_head_dims_128_192(d, q_dtype, entry, splits):
+    window = 300 if q_dtype == "e4m3" else -1
+    if entry == "decode":     # GQA 8:1, q_len 1..16, ragged lengths
+        w = wl.custom(q_dtype, d, 16, 2, window, [700, 65, 1500], [4, 16, 1], seed=d + 1)
+    else:                     # several 256-row q blocks, ragged tails, chunked prefill
+        w = wl.custom(q_dtype, d, 8, 2, window, [600, 90, 1300], [300, 90, 41], seed=d + 2)
+    log(f"[case] head dim {d} {q_dtype} {entry} splits={splits}")
+    o_ref, l_ref, codes_ref = oracle_run(w)
+    o, l, codes, s = gpu_run(w, entry, num_splits=splits)
+    if codes is not None:
+        assert np.array_equal(codes, codes_ref)
+    compare(o, o_ref, l, l_ref, label=f"d{d} {q_dtype} {entry} S={s}")
+    if q_dtype == "e4m3":
+        o1, l1, _, s1 = gpu_run(w, entry, num_splits=splits, fused_q=True)
+        assert s1 == s and np.array_equal(o1, o) and np.array_equal(l1, l)
 
 
 def test_page_size_128_and_strided_output():

@@ -185,6 +185,48 @@ def time_workload(make, entry, nsets, steps, warmup, label, fused=True):
     return out
 
 
+def time_graph(make, entry, nsets, steps, label, fused=True):
+    """The same steps captured in one HIP graph (one attention call per input set, the split-KV
+    combine included) and replayed back to back: HIP events around the replays, per step."""
+    import torch
+    runners = [Runner(make(seed), entry, fused) for seed in range(nsets)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm-up on a side stream, as capture requires
+        for r in runners:
+            r.quantize(side.cuda_stream)
+            r.attend(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream().cuda_stream
+        for r in runners:
+            r.quantize(cs)
+            r.attend(cs)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // nsets)
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / (reps * nsets)
+    w = runners[0].w
+    tb, _ = algo_bytes(w, fused)
+    log(f"[bench] {label}: graph replay {ms:.4f} ms per step")
+    out = {"workload": w.name, "graph_ms_per_step": round(ms, 4), "steps_per_graph": nsets,
+           "splits": runners[0].splits, "kv_read_GBps": round(tb / (ms * 1e-3) / 1e9, 1),
+           "hbm_frac": round(tb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del runners, g
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_cache_write(make, steps, label):
     """The KV-cache write of a workload's new tokens (bf16 K/V for every new token and kv head,
     stored at the tokens' slots in the workload's pools), timed with events around `steps`
@@ -376,6 +418,9 @@ def main():
                 peak = FP8_PEAK_TFLOPS if ww.q_dtype == "e4m3" else BF16_PEAK_TFLOPS
                 e["mfma_frac"] = round(e["TFLOPs"] / peak, 4)
             extra[name] = e
+        for name, make, ns in [("swa_decode_graph", lambda s: wl.swa_decode(device="cuda", seed=100 + s), nsets),
+                               ("full_decode_graph", lambda s: wl.full_decode(device="cuda", seed=200 + s), 4)]:
+            extra[name] = time_graph(make, "decode", ns, max(8, args.steps), name, fused)
         for name, make in [("kv_write_swa_prefill", lambda s: wl.swa_prefill(device="cuda", seed=400 + s)),
                            ("kv_write_swa_decode", lambda s: wl.swa_decode(device="cuda", seed=100 + s))]:
             extra[name] = time_cache_write(make, max(5, args.steps // 5), name)

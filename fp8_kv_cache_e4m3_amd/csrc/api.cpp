@@ -183,11 +183,22 @@ fp8attn::AttnParams make_params(const fp8attn_attn_args* a) {
 struct DecodePlan {
   int32_t row_groups;
   int32_t max_units;
-  int32_t splits;
+  int32_t splits;            // split count, or minus the partition count (balanced partition)
   int32_t units_per_split;
+  bool balanced;
   size_t ws_bytes;
   int64_t grid;
 };
+
+// Automatic mode takes the balanced partition for long key ranges with one row tile per
+// sequence: there a spread of lengths leaves most compute units idle behind the longest sequence
+// (B64 d512, lengths U[8K, 32K]: 1.04 ms at one split against 0.87 ms for the same bytes at
+// equal lengths), and more splits cost more than they balance (1.14 ms at 16).  Short ranges
+// (a 1024-key window) are uniform by construction and keep the one-kernel plan; several row
+// tiles per sequence (spec-decode verify) keep theirs, because the split grid runs a
+// sequence's tiles side by side and they share its K/V in L2.
+constexpr int32_t kBalancedMinUnits = 256;   // 4096 keys
+constexpr int32_t kMaxParts = 1 << 20;
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -207,11 +218,23 @@ DecodePlan plan_decode(const fp8attn_attn_args* a, int32_t requested) {
   if (a->window >= 1) vis = std::min<int64_t>(vis, (int64_t)a->window + a->max_seqlen_q - 1);
   pl.max_units = (int32_t)((vis + 15) / 16 + 1);
   const int64_t items = (int64_t)a->num_kv_heads * a->batch * pl.row_groups;
+  const int64_t per_cu = a->head_dim > 256 ? 1 : a->head_dim > 64 ? 2 : 4;
+  if (requested < 0 || (requested == 0 && pl.row_groups == 1 && pl.max_units >= kBalancedMinUnits)) {
+    // balanced partition into R parts: one block per part, all resident at once in automatic mode
+    const int64_t R = requested < 0 ? -(int64_t)requested : (int64_t)cu_count() * per_cu;
+    const size_t slots = (size_t)R + (size_t)items;
+    pl.balanced = true;
+    pl.splits = (int32_t)-R;
+    pl.units_per_split = 0;
+    pl.ws_bytes = round_up(slots * 16 * a->head_dim * sizeof(float)) + round_up(slots * 16 * sizeof(float)) +
+                  round_up((size_t)items * 2 * sizeof(int32_t));
+    pl.grid = R;
+    return pl;
+  }
   int64_t S;
   if (requested > 0) {
     S = requested;
   } else {
-    const int64_t per_cu = a->head_dim > 256 ? 1 : a->head_dim > 64 ? 2 : 4;
     const int64_t resident = (int64_t)cu_count() * per_cu;
     S = (resident + items - 1) / items;
     S = std::min<int64_t>(S, std::max<int64_t>(1, pl.max_units / 32));
@@ -321,7 +344,9 @@ fp8attn_status fp8attn_decode_paged(const fp8attn_attn_args* args, int32_t num_s
   const char* fn = "fp8attn_decode_paged";
   fp8attn_status st = validate_attn(fn, args, true);
   if (st != FP8ATTN_OK) return st;
-  if (num_splits < 0) return fail(FP8ATTN_ERR_INVALID_ARG, "%s: num_splits must be >= 0 (0 = automatic)", fn);
+  if (num_splits < -kMaxParts)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: num_splits %d: a balanced partition takes at most %d parts", fn,
+                num_splits, kMaxParts);
   if (args->total_q == 0 || args->batch == 0) {
     if (workspace_needed) *workspace_needed = 0;
     if (num_splits_used) *num_splits_used = 1;
@@ -331,26 +356,46 @@ fp8attn_status fp8attn_decode_paged(const fp8attn_attn_args* args, int32_t num_s
   if (workspace_needed) *workspace_needed = pl.ws_bytes;
   if (num_splits_used) *num_splits_used = pl.splits;
   if (!workspace && workspace_needed) return ok();  // size query
+  if (pl.balanced &&
+      (int64_t)args->num_kv_heads * args->batch * pl.row_groups + pl.grid >= (int64_t)1 << 31)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: %lld row tiles are too many for a balanced partition", fn,
+                (long long)args->num_kv_heads * args->batch * pl.row_groups);
   if (pl.grid >= (int64_t)1 << 31)
     return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: grid of %lld blocks is too large", fn, (long long)pl.grid);
   fp8attn::AttnParams p = make_params(args);
   p.num_splits = pl.splits;
   p.units_per_split = pl.units_per_split;
   p.row_groups = pl.row_groups;
-  if (pl.splits > 1) {
+  if (pl.ws_bytes > 0) {
     if (!workspace || workspace_bytes < pl.ws_bytes)
-      return fail(FP8ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %d splits, got %zu", fn,
-                  pl.ws_bytes, pl.splits, workspace ? workspace_bytes : (size_t)0);
+      return fail(FP8ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %s %d, got %zu", fn,
+                  pl.ws_bytes, pl.balanced ? "a balanced partition of parts" : "split count",
+                  pl.balanced ? -pl.splits : pl.splits, workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, kAlign))
       return fail(FP8ATTN_ERR_INVALID_ARG, "%s: workspace must be %zu-byte aligned", fn, kAlign);
+  }
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (pl.balanced) {
+    const size_t items = (size_t)args->num_kv_heads * args->batch * pl.row_groups;
+    const size_t slots = (size_t)pl.grid + items;
+    p.part_o = reinterpret_cast<float*>(ws);
+    p.part_lse = reinterpret_cast<float*>(ws + round_up(slots * 16 * args->head_dim * sizeof(float)));
+    p.seg_meta = reinterpret_cast<int32_t*>(ws + round_up(slots * 16 * args->head_dim * sizeof(float)) +
+                                            round_up(slots * 16 * sizeof(float)));
+  } else if (pl.splits > 1) {
     const size_t rows = (size_t)args->total_q * args->num_q_heads;
-    p.part_o = reinterpret_cast<float*>(workspace);
-    p.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                          round_up((size_t)pl.splits * rows * args->head_dim * sizeof(float)));
+    p.part_o = reinterpret_cast<float*>(ws);
+    p.part_lse = reinterpret_cast<float*>(ws + round_up((size_t)pl.splits * rows * args->head_dim * sizeof(float)));
   }
   hipError_t e = fp8attn::launch_decode(p, args->q_dtype, args->head_dim, pl.grid, stream);
   if (e != hipSuccess) return hip_fail(fn, e);
-  if (pl.splits > 1) {
+  if (pl.balanced) {
+    e = fp8attn::launch_combine_parts(p.part_o, p.part_lse, p.seg_meta, args->cu_seqlens_q, args->batch,
+                                      pl.row_groups, args->num_kv_heads, args->num_q_heads / args->num_kv_heads,
+                                      (int32_t)pl.grid, args->head_dim, args->out, args->out_stride_tok, args->out_stride_head,
+                                      args->lse, stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  } else if (pl.splits > 1) {
     e = fp8attn::launch_combine(p.part_o, p.part_lse, pl.splits, args->total_q, args->num_q_heads, args->head_dim,
                                 args->out, args->out_stride_tok, args->out_stride_head, args->lse, stream);
     if (e != hipSuccess) return hip_fail(fn, e);

@@ -116,9 +116,13 @@ struct QRegs<true, D> { uint64_t q[2 * DecodeShape<D>::KCH]; };
 template <int D>
 struct QRegs<false, D> { bf16x8_t q[2 * DecodeShape<D>::KCH]; };
 
-template <int QM, int D>
-__global__ void __launch_bounds__(256)
-    __attribute__((amdgpu_waves_per_eu(DecodeTune<QM != kQBf16, D>::MIN_WAVES))) decode_kernel(const AttnParams p) {
+// One 16-row query tile: row tile rt of sequence b under kv head h, over units
+// [u_begin + o0, u_begin + o1) of the tile's visible unit range [u_begin, u_end).  whole: the
+// segment is the tile's whole range, so O and LSE are final and go to the output; otherwise the
+// tile writes fp32 partials to entry pidx (a split index, or a slot of the balanced partition).
+template <int QM, int D, bool BAL>
+__device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, const int h, const int rt,
+                                            const int o0, const int o1, const int pidx, const bool whole) {
   constexpr bool QFP8 = QM != kQBf16;   // QK^T on the FP8 MFMA
   using S = DecodeShape<D>;
   using T = DecodeTune<QFP8, D>;
@@ -130,14 +134,6 @@ __global__ void __launch_bounds__(256)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
-
-  // ---- work item (32-bit index arithmetic: the host keeps the grid below 2^31) ----------
-  uint32_t id = xcd_remap32(blockIdx.x, gridDim.x);
-  const uint32_t n_rt = (uint32_t)p.row_groups, n_b = (uint32_t)p.batch, n_s = (uint32_t)p.num_splits;
-  const int rt = (int)(id % n_rt); id /= n_rt;
-  const int b = (int)(id % n_b); id /= n_b;
-  const int s = (int)(id % n_s);
-  const int h = (int)(id / n_s);
   const int G = p.group;
 
   // Every per-item scalar of the prologue is requested here, before any branch, so that the
@@ -164,8 +160,8 @@ __global__ void __launch_bounds__(256)
   const int k_lo = W >= 1 ? max(0, p_first - W + 1) : 0;
   const int u_begin = k_lo / 16;
   const int u_end = (p_last + 16) / 16;              // ceil((p_last + 1) / 16)
-  const int su0 = u_begin + s * p.units_per_split;
-  const int su1 = min(u_end, su0 + p.units_per_split);
+  const int su0 = u_begin + o0;
+  const int su1 = min(u_end, u_begin + o1);
   // keys every row of this tile can see: [full_lo, p_first]
   const int full_lo = W >= 1 ? p_last - W + 1 : 0;
 
@@ -177,8 +173,9 @@ __global__ void __launch_bounds__(256)
   const int pos = L - ql + tok;
 
   if (su0 >= su1) {  // nothing visible in this split: neutral partial for the combine
-    if (p.num_splits > 1 && threadIdx.x < 16 && rvalid)
-      p.part_lse[((int64_t)s * p.total_q + t0 + tok) * p.hq + hq] = kNegInf;
+    // (a segment of the balanced partition is never empty)
+    if (!BAL && !whole && threadIdx.x < 16 && rvalid)
+      p.part_lse[((int64_t)pidx * p.total_q + t0 + tok) * p.hq + hq] = kNegInf;
     return;
   }
 
@@ -417,7 +414,7 @@ __global__ void __launch_bounds__(256)
       const int hh = h * G + rr % G;
       const float inv = Ls > 0.f ? vd / Ls : 0.f;
       const float lse2 = Ls > 0.f ? (M + fast_log2(Ls)) : kNegInf;
-      if (p.num_splits == 1) {
+      if (whole) {
         __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)tk * p.out_stride_tok +
                      (int64_t)hh * p.out_stride_head + part * PW;
 #pragma unroll
@@ -431,7 +428,9 @@ __global__ void __launch_bounds__(256)
         }
         if (p.lse && part == 0) p.lse[(int64_t)tk * p.hq + hh] = lse2 * kLn2;
       } else {
-        float* op = p.part_o + (((int64_t)s * p.total_q + tk) * p.hq + hh) * D + part * PW;
+        // split: [split, token, q head]; balanced partition: [slot, tile row]
+        const int64_t e = BAL ? (int64_t)pidx * 16 + row : ((int64_t)pidx * p.total_q + tk) * p.hq + hh;
+        float* op = p.part_o + e * D + part * PW;
 #pragma unroll
         for (int c = 0; c < PW; c += 4) {
           f32x4_t a = *reinterpret_cast<const f32x4_t*>(&sm_o[0][row][part * PW + c]);
@@ -439,33 +438,169 @@ __global__ void __launch_bounds__(256)
           for (int w = 1; w < 4; ++w) a += *reinterpret_cast<const f32x4_t*>(&sm_o[w][row][part * PW + c]);
           *reinterpret_cast<f32x4_t*>(op + c) = a * inv;
         }
-        if (part == 0) p.part_lse[((int64_t)s * p.total_q + tk) * p.hq + hh] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
+        if (part == 0) p.part_lse[e] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
       }
     }
   }
+  // a block of the balanced partition runs several tiles in turn: the next tile's merge must not
+  // overwrite the LDS this one is still reading
+  if constexpr (BAL) __syncthreads();
 }
 
-template <int QM>
+// Split grid: one block per (kv head, split, sequence, row tile), XCD-aware order.
+template <int QM, int D>
+__global__ void __launch_bounds__(256)
+    __attribute__((amdgpu_waves_per_eu(DecodeTune<QM != kQBf16, D>::MIN_WAVES))) decode_kernel(const AttnParams p) {
+  // (32-bit index arithmetic: the host keeps the grid below 2^31)
+  uint32_t id = xcd_remap32(blockIdx.x, gridDim.x);
+  const uint32_t n_rt = (uint32_t)p.row_groups, n_b = (uint32_t)p.batch, n_s = (uint32_t)p.num_splits;
+  const int rt = (int)(id % n_rt); id /= n_rt;
+  const int b = (int)(id % n_b); id /= n_b;
+  const int s = (int)(id % n_s);
+  const int h = (int)(id / n_s);
+  const int o0 = s * p.units_per_split;
+  decode_tile<QM, D, false>(p, b, h, rt, o0, o0 + p.units_per_split, s, p.num_splits == 1);
+}
+
+// ---- balanced partition ----------------------------------------------------------------------
+// The row tiles' visible 16-key units, laid end to end in (kv head, sequence, row tile) order,
+// form one stream of T units; block i of R = min(grid, T) takes units [i T / R, (i + 1) T / R).
+// Every block then streams the same number of units (within one), whatever the mix of sequence
+// lengths, and each block pays one pipeline fill and drain instead of one per split.  A block's
+// range cuts into tiles: a tile whose range lies inside one block is final there; a tile cut by
+// block boundaries leaves one fp32 partial per block in slot (block + tile index), and records
+// the first and last block of its range for the combine.  The unit counts come from the device
+// lengths (every block recomputes them, a wave-wide prefix sum per 64 tiles), so the host plans
+// from the grid size and the shapes alone.
+
+// Units of row tile rt of sequence b: the range decode_tile walks for that tile.
+__device__ __forceinline__ uint32_t tile_units(const AttnParams& p, int b, int rt) {
+  const int t0 = p.cu_seqlens_q[b], t1 = p.cu_seqlens_q[b + 1], L = p.seqlens_k[b];
+  const int ql = t1 - t0, nrows = ql * p.group, row0 = rt * 16;
+  if (row0 >= nrows) return 0u;
+  const int rlast = min(row0 + 16, nrows) - 1;
+  const int p_first = L - ql + row0 / p.group, p_last = L - ql + rlast / p.group;
+  const int k_lo = p.window >= 1 ? max(0, p_first - p.window + 1) : 0;
+  return (uint32_t)max(0, (p_last + 16) / 16 - k_lo / 16);
+}
+
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, (unsigned)o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// 64 consecutive row tiles (tile index j = sequence * row_groups + row tile), one per lane
+struct TileChunk {
+  int base;          // first tile of the chunk
+  uint32_t acc;      // units of the tiles before the chunk (within one kv head)
+  uint32_t n, incl;  // this lane's tile: units, inclusive prefix within the chunk
+  uint32_t total;    // units of the chunk
+};
+
+__device__ __forceinline__ TileChunk load_chunk(const AttnParams& p, int base, uint32_t acc, int J) {
+  TileChunk c;
+  c.base = base;
+  c.acc = acc;
+  const int j = base + (int)(threadIdx.x & 63);
+  c.n = j < J ? tile_units(p, j / p.row_groups, j % p.row_groups) : 0u;
+  c.incl = wave_inclusive_sum(c.n);
+  c.total = (uint32_t)__builtin_amdgcn_readlane((int)c.incl, 63);
+  return c;
+}
+
+// Wave-uniform values computed on the vector ALU (64-bit division) are moved back to scalar
+// registers, so that the loop state around a tile costs no vector registers.
+__device__ __forceinline__ uint32_t to_sgpr(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+__device__ __forceinline__ uint64_t to_sgpr(uint64_t x) {
+  return (uint64_t)to_sgpr((uint32_t)x) | ((uint64_t)to_sgpr((uint32_t)(x >> 32)) << 32);
+}
+
+template <int QM, int D>
+__global__ void __launch_bounds__(256)
+    __attribute__((amdgpu_waves_per_eu(DecodeTune<QM != kQBf16, D>::MIN_WAVES)))
+    decode_balanced_kernel(const AttnParams p) {
+  const uint32_t i = xcd_remap32(blockIdx.x, gridDim.x);
+  const int J = p.batch * p.row_groups;          // row tiles per kv head
+  uint32_t t_head = 0;
+  for (int base = 0; base < J; base += 64) t_head += load_chunk(p, base, 0u, J).total;
+  t_head = to_sgpr(t_head);
+  const uint64_t T = (uint64_t)t_head * (uint32_t)p.hkv;
+  // At most T parts, so that every part holds a unit and the blocks of a tile's range are
+  // consecutive (the combine walks them from first to last); blocks past that have no work.
+  const uint32_t R = (uint32_t)(T < gridDim.x ? T : gridDim.x);
+  if (i >= R) return;
+  const uint64_t start = to_sgpr((uint64_t)i * T / R), end = to_sgpr((uint64_t)(i + 1) * T / R);
+  // Only the chunk's position stays live across a tile (its per-lane counts are loaded again for
+  // the next segment), which keeps the tile's register budget.
+  int c_base = 0;
+  uint32_t c_acc = 0;
+  for (uint64_t u = start; u < end;) {
+    const int h = (int)to_sgpr((uint32_t)(u / t_head));
+    const uint32_t rem = (uint32_t)(u - (uint64_t)h * t_head);
+    if (rem < c_acc) c_base = 0, c_acc = 0;        // the next kv head starts over at tile 0
+    TileChunk c = load_chunk(p, c_base, c_acc, J);
+    while (rem >= c.acc + c.total && c.base + 64 < J) c = load_chunk(p, c.base + 64, c.acc + c.total, J);
+    c_base = c.base;
+    c_acc = c.acc;
+    // the tile holding unit rem: the first lane whose inclusive prefix passes it
+    const int idx = (int)__popcll(__ballot(c.acc + c.incl <= rem));
+    const int j = c.base + idx;
+    if (idx >= 64 || j >= J) break;   // (only if the lengths changed under the kernel)
+    const uint32_t n_j = (uint32_t)__builtin_amdgcn_readlane((int)c.n, idx);
+    const uint32_t u_j = c.acc + (uint32_t)__builtin_amdgcn_readlane((int)c.incl, idx) - n_j;
+    const uint64_t lo = (uint64_t)h * t_head + u_j, hi = lo + n_j;
+    const uint64_t seg_end = hi < end ? hi : end;
+    if (seg_end <= u) break;
+    const int o0 = (int)(u - lo), o1 = (int)(seg_end - lo);
+    const int g = h * J + j;
+    if (o0 == 0 && threadIdx.x == 0) {   // the tile's first segment: blocks of its first and last unit
+      p.seg_meta[2 * g] = (int32_t)i;
+      p.seg_meta[2 * g + 1] = (int32_t)((hi * R - 1) / T);
+    }
+    decode_tile<QM, D, true>(p, j / p.row_groups, h, j % p.row_groups, o0, o1, (int)i + g,
+                             o0 == 0 && seg_end == hi);
+    u = to_sgpr(seg_end);
+  }
+}
+
+template <int QM, bool BAL>
 static void launch_decode_dims(const AttnParams& p, int head_dim, dim3 g, hipStream_t stream) {
   const dim3 blk(256);
+#define FP8ATTN_DECODE(DIM)                                                                  \
+  do {                                                                                       \
+    if constexpr (BAL) hipLaunchKernelGGL((decode_balanced_kernel<QM, DIM>), g, blk, 0, stream, p); \
+    else hipLaunchKernelGGL((decode_kernel<QM, DIM>), g, blk, 0, stream, p);                 \
+  } while (0)
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL((decode_kernel<QM, 64>), g, blk, 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((decode_kernel<QM, 128>), g, blk, 0, stream, p); break;
-    case 192: hipLaunchKernelGGL((decode_kernel<QM, 192>), g, blk, 0, stream, p); break;
+    case 64: FP8ATTN_DECODE(64); break;
+    case 128: FP8ATTN_DECODE(128); break;
+    case 192: FP8ATTN_DECODE(192); break;
     default:
       // the last head dim of each variant: 256 (FP8 Q) or 512 (BF16 Q)
-      if constexpr (QM == kQBf16) hipLaunchKernelGGL((decode_kernel<QM, 512>), g, blk, 0, stream, p);
-      else hipLaunchKernelGGL((decode_kernel<QM, 256>), g, blk, 0, stream, p);
+      if constexpr (QM == kQBf16) FP8ATTN_DECODE(512);
+      else FP8ATTN_DECODE(256);
   }
+#undef FP8ATTN_DECODE
+}
+
+template <bool BAL>
+static void launch_decode_modes(const AttnParams& p, int q_mode, int head_dim, dim3 g, hipStream_t stream) {
+  if (q_mode == kQE4M3) launch_decode_dims<kQE4M3, BAL>(p, head_dim, g, stream);
+  else if (q_mode == kQBf16E4M3) launch_decode_dims<kQBf16E4M3, BAL>(p, head_dim, g, stream);
+  else launch_decode_dims<kQBf16, BAL>(p, head_dim, g, stream);
 }
 
 hipError_t launch_decode(const AttnParams& p, int q_mode, int head_dim, int64_t grid,
                          hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   const dim3 g((unsigned)grid);
-  if (q_mode == kQE4M3) launch_decode_dims<kQE4M3>(p, head_dim, g, stream);
-  else if (q_mode == kQBf16E4M3) launch_decode_dims<kQBf16E4M3>(p, head_dim, g, stream);
-  else launch_decode_dims<kQBf16>(p, head_dim, g, stream);
+  if (p.seg_meta) launch_decode_modes<true>(p, q_mode, head_dim, g, stream);
+  else launch_decode_modes<false>(p, q_mode, head_dim, g, stream);
   return hipGetLastError();
 }
 

@@ -38,6 +38,10 @@ struct AttnParams {
   int32_t max_seqlen_q;
   float* part_o;                               // fp32 [S, total_q, hq, d] when S > 1
   float* part_lse;                             // fp32 [S, total_q, hq]
+  // balanced partition (non-NULL selects it; the grid is the partition count R):
+  // part_o [R + hkv * batch * row_groups, 16, d], part_lse [same, 16],
+  // seg_meta [hkv * batch * row_groups][2] = first and last block of each row tile's range
+  int32_t* seg_meta;
 };
 
 // How the kernels receive Q (values of fp8attn_dtype)
@@ -68,7 +72,8 @@ hipError_t launch_quantize_q(const void* q, int64_t ntok, int32_t nheads, int32_
                              int64_t stride_tok, int64_t stride_head, const float* q_descale,
                              void* out, hipStream_t stream);
 
-// Split-KV paged attention over 16-row query tiles.  grid = row_groups * batch * S * hkv.
+// Split-KV paged attention over 16-row query tiles.  grid = row_groups * batch * S * hkv, or
+// the partition count R when p.seg_meta is set (balanced partition).
 hipError_t launch_decode(const AttnParams& p, int q_mode, int head_dim, int64_t grid,
                          hipStream_t stream);
 
@@ -79,5 +84,12 @@ hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, bool q_bf16, hi
 hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t S, int64_t total_q,
                           int32_t hq, int32_t d, void* out, int64_t out_stride_tok,
                           int64_t out_stride_head, float* lse_out, hipStream_t stream);
+
+// Combine of the balanced partition (decode with p.seg_meta set): merges the row tiles whose
+// range spans several blocks; the others were written final by the decode kernel.
+hipError_t launch_combine_parts(const float* part_o, const float* part_lse, const int32_t* seg_meta,
+                                const int32_t* cu_seqlens_q, int32_t batch, int32_t row_groups, int32_t hkv,
+                                int32_t group, int32_t parts, int32_t d, void* out, int64_t out_stride_tok,
+                                int64_t out_stride_head, float* lse_out, hipStream_t stream);
 
 }  // namespace fp8attn

@@ -167,6 +167,35 @@ def test_decode_workspace_query_needs_no_gpu_reads():
     assert st == fa.ERR_WORKSPACE and "workspace" in fa.fp8attn_last_error()
 
 
+def test_decode_balanced_partition_plan():
+    # num_splits = -R asks for the balanced partition into R parts; automatic mode takes it for
+    # long key ranges with one 16-row tile per sequence (planned from host values only)
+    a, keep = _valid_args()
+    need, used = ctypes.c_size_t(0), ctypes.c_int32(0)
+
+    def query(n):
+        st = fa.LIB.fp8attn_decode_paged(ctypes.byref(a), n, None, 0, ctypes.byref(need), ctypes.byref(used), None)
+        assert st == fa.OK, fa.fp8attn_last_error()
+        return used.value, need.value
+
+    u, n = query(-5)
+    items = 2 * 2 * 1                      # kv heads x sequences x row tiles
+    slots = 5 + items
+    assert u == -5 and n >= slots * 16 * 512 * 4 + slots * 16 * 4 + items * 8
+    assert query(0)[0] > 0                 # 200 keys: the split plan
+    a.max_seqlen_k = 8192
+    a.block_table_stride = 128
+    assert query(0)[0] < 0                 # 8192 keys, 8 rows per sequence: balanced
+    a.max_seqlen_q = 5                     # 20 rows per sequence: two row tiles, split plan
+    assert query(0)[0] > 0
+    a.max_seqlen_q = 2
+    st = fa.LIB.fp8attn_decode_paged(ctypes.byref(a), -(1 << 20) - 1, None, 0, ctypes.byref(need), None, None)
+    assert st == fa.ERR_INVALID_ARG and "balanced" in fa.fp8attn_last_error()
+    buf = torch.zeros(64, dtype=torch.uint8)
+    st = fa.LIB.fp8attn_decode_paged(ctypes.byref(a), -5, buf.data_ptr(), 64, None, None, None)
+    assert st == fa.ERR_WORKSPACE and "balanced" in fa.fp8attn_last_error()
+
+
 def test_cache_write_rejections():
     L = fa.LIB
     args = lambda **kw: {**dict(k=None, v=None, T=4, H=2, d=32, kst=64, ksh=32, vst=64, vsh=32, slots=None,

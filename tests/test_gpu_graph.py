@@ -22,14 +22,15 @@ def _fa():
     return fa
 
 
-@pytest.mark.parametrize("q_dtype,d,hq,hkv,window,q_len,fused", [
-    ("e4m3", 256, 32, 16, 1024, 1, True),    # sliding-window layer, bf16 Q quantized in-kernel
-    ("bf16", 512, 32, 4, -1, 1, False),      # full-attention layer
-    ("bf16", 512, 32, 4, -1, 4, False),      # spec-decode verify (4 query tokens)
+@pytest.mark.parametrize("q_dtype,d,hq,hkv,window,q_len,fused,cap", [
+    ("e4m3", 256, 32, 16, 1024, 1, True, 3000),    # sliding-window layer, bf16 Q quantized in-kernel
+    ("bf16", 512, 32, 4, -1, 1, False, 3000),      # full-attention layer, split plan
+    ("bf16", 512, 32, 4, -1, 1, False, 6000),      # full-attention layer, balanced partition
+    ("bf16", 512, 32, 4, -1, 4, False, 3000),      # spec-decode verify (4 query tokens)
 ])
-def test_graph_replay_with_changing_lengths(q_dtype, d, hq, hkv, window, q_len, fused):
+def test_graph_replay_with_changing_lengths(q_dtype, d, hq, hkv, window, q_len, fused, cap):
     fa = _fa()
-    B, cap = 4, 3000                          # key-length bound fixed at capture
+    B = 4                                    # cap: the key-length bound fixed at capture
     base = wl.custom(q_dtype, d, hq, hkv, window, [cap] * B, [q_len] * B, seed=61)
     dev = torch.device("cuda")
     wd = base.to(dev)
@@ -49,10 +50,11 @@ def test_graph_replay_with_changing_lengths(q_dtype, d, hq, hkv, window, q_len, 
                                        window=window, out=o, lse=l, workspace=ws, quantize_q=fused)
 
     # workspace sized once, outside the capture
-    _, _, splits = call(torch.empty_like(out), torch.empty_like(lse))
-    assert splits > 1, "the case should exercise the combine inside the graph"
-    rows = T * hq
-    ws = torch.empty(2 * splits * rows * (d + 1) * 4 + 4096, dtype=torch.uint8, device=dev)
+    a = fa.make_args(q_s, wd.k_pool, wd.v_pool, bt_s, wd.cu_seqlens_q, sk_s, q_len, cap, qd, wd.k_descale,
+                     wd.v_descale, 0.0, window, True, out, lse, quantize_q=fused)
+    need, splits = fa.decode_workspace_size(a, 0)
+    assert splits != 1, "the case should exercise the combine inside the graph"
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):             # warm-up on the capture stream

@@ -152,15 +152,44 @@ def test_fused_q_full_size_swa_decode():
 # ------------------------------------------------------------------------------------------
 # split-KV: every split count meets the bar; one split needs no workspace
 # ------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("splits", [1, 2, 3, 7, 0, 1000])
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 0, 1000, -1, -2, -7, -64, -1000])
 def test_split_counts(splits):
+    # negative: the balanced partition into -splits parts (more parts than units included)
     w = wl.custom("bf16", 512, 8, 2, -1, [700, 64, 1500, 3], [1, 2, 1, 3], seed=21)
     o_ref, l_ref, _ = oracle_run(w)
     o, l, _, used = gpu_run(w, "decode", num_splits=splits)
     log(f"[case] splits requested={splits} used={used}")
     if splits > 0:
         assert 1 <= used <= splits
+    elif splits < 0:
+        assert used == splits
     compare(o, o_ref, l, l_ref, label=f"splits={splits}->{used}")
+
+
+# ------------------------------------------------------------------------------------------
+# balanced partition: the batch's units split evenly over the blocks, tiles cut by block
+# boundaries merged by the partition's combine
+# ------------------------------------------------------------------------------------------
+_R25 = [int(x) for x in np.random.default_rng(9).integers(16, 3000, 25)]
+
+
+@pytest.mark.parametrize("q_dtype,d,hq,hkv,window,seqlens,qlens,parts,fused", [
+    ("bf16", 512, 32, 4, -1, [9000, 300, 4100, 17, 2000], [1, 1, 1, 1, 1], 0, False),   # automatic pick
+    ("bf16", 512, 8, 2, -1, [700, 64, 1500, 16, 999], [1, 2, 1, 3, 16], -5, False),      # ragged q_len
+    ("e4m3", 256, 32, 16, 1024, [5000, 1030, 17, 3000], [1, 1, 1, 1], -37, True),      # window, fused Q
+    ("e4m3", 64, 16, 1, -1, [2000] * 70, [1] * 70, -100, True),                       # 70 tiles: two chunks
+    ("bf16", 128, 8, 1, 77, [400, 90, 1300], [16, 3, 9], -3, False),                   # 8 row tiles, window
+    ("bf16", 64, 16, 2, -1, _R25, [16] * 25, -50, False),                              # 200 tiles per kv head
+])
+def test_balanced_partition(q_dtype, d, hq, hkv, window, seqlens, qlens, parts, fused):
+    w = wl.custom(q_dtype, d, hq, hkv, window, seqlens, qlens, seed=71)
+    log(f"[case] balanced {q_dtype} d{d} {hq}/{hkv} W{window} B{len(seqlens)} parts={parts}")
+    o_ref, l_ref, _ = oracle_run(w)
+    o, l, _, used = gpu_run(w, "decode", num_splits=parts, fused_q=fused)
+    assert used < 0 and (parts == 0 or used == parts), used
+    compare(o, o_ref, l, l_ref, label=f"balanced parts={-used}")
+    o2, l2, _, _ = gpu_run(w, "decode", num_splits=parts, fused_q=fused)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2), "two identical runs differ"
 
 
 def test_combine_entry_point():

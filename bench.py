@@ -40,6 +40,8 @@ KERNEL_SOURCES = {
                "fp8_kv_cache_e4m3_amd/csrc/params.h"],
     "prefill": ["fp8_kv_cache_e4m3_amd/csrc/prefill.hip", "fp8_kv_cache_e4m3_amd/csrc/device.h",
                 "fp8_kv_cache_e4m3_amd/csrc/params.h"],
+    "combine": ["fp8_kv_cache_e4m3_amd/csrc/combine.hip", "fp8_kv_cache_e4m3_amd/csrc/device.h",
+                "fp8_kv_cache_e4m3_amd/csrc/params.h"],
 }
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -412,6 +414,11 @@ def main():
                  "attention_ms": round(r["kernel_ms"], 4), "splits": r["splits"],
                  "kv_read_GBps": round(tb / (r["kernel_ms"] * 1e-3) / 1e9, 1),
                  "TFLOPs": round(fl / (r["kernel_ms"] * 1e-3) / 1e12, 2)}
+            # HBM bytes of the step's kernels (decode plus the partition's combine; both prefill instances)
+            keys = {"full_decode": ["decode_full", "decode_full_combine"], "spec_verify": ["decode_spec"],
+                    "swa_prefill": ["prefill_swa", "prefill_swa_splitp"]}[name]
+            tr = [load_traffic(k) for k in keys]
+            e["traffic"] = sum(tr) if fused and all(t is not None for t in tr) else None
             if bound == "hbm":
                 e["hbm_frac"] = round(e["kv_read_GBps"] / HBM_PEAK_GBS, 4)
             else:

@@ -232,8 +232,10 @@ def fp8attn_decode_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens
                          q_descale=None, k_descale=None, v_descale=None, softmax_scale=0.0, window=-1,
                          causal=True, out=None, lse=None, want_lse=True, num_splits=0, workspace=None,
                          descale_strides=(0, 0), quantize_q=False, stream=None):
-    """Returns (out, lse, splits_used).  The workspace is sized by a query and allocated with torch
-    if the caller passes none.  quantize_q: bf16 q is quantized to E4M3 inside the call."""
+    """Returns (out, lse, splits_used).  num_splits: 0 automatic, N > 0 that many splits, -R the
+    balanced partition into R parts (splits_used is then -R).  The workspace is sized by a query
+    and allocated with torch if the caller passes none.  quantize_q: bf16 q is quantized to E4M3
+    inside the call."""
     out, lse = _alloc_out(q, out, lse, want_lse)
     a = make_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seqlen_k,
                   q_descale, k_descale, v_descale, softmax_scale, window, causal, out, lse, descale_strides,

@@ -141,12 +141,20 @@ fp8attn_status fp8attn_prefill_varlen(const fp8attn_attn_args* args, hipStream_t
  * Paged attention for few new tokens per sequence (decode, spec-decode verify), with split-KV
  * over the key range and a log-sum-exp combine ([60372] Claims: the split count is picked
  * automatically, with no fixed cap).  max_seqlen_q must be <= 16.
- *   num_splits      : 0 = automatic; otherwise the requested count (clamped to the key range)
- *   workspace       : device scratch for split partials; NULL with workspace_needed != NULL is a
- *                     size query that launches nothing
- *   workspace_needed: out, bytes needed for the chosen split count (may be NULL)
- *   num_splits_used : out, the split count chosen (may be NULL)
- * With one split no workspace is needed and the output is written directly.
+ *   num_splits      : 0 = automatic; N > 0 = N splits per (sequence, kv head, 16-row tile),
+ *                     clamped to the key range; -R = the balanced partition into R parts
+ *                     (R <= 2^20): the visible 16-key units of all tiles, laid end to end, are
+ *                     cut into R equal ranges, one per thread block, so that every block streams
+ *                     the same number of keys whatever the mix of sequence lengths
+ *   workspace       : device scratch for partials; NULL with workspace_needed != NULL is a
+ *                     size query that launches nothing.  256-byte aligned
+ *   workspace_needed: out, bytes needed for the chosen plan (may be NULL)
+ *   num_splits_used : out, the split count chosen, or -R for a balanced partition (may be NULL)
+ * Automatic mode takes the balanced partition (R = blocks resident on the device at once) when
+ * every sequence's rows fit one 16-row tile and max_seqlen_k (or the window) spans at least
+ * 4096 keys; otherwise it takes just enough splits to fill the device once.  Planning reads host
+ * values only (the call is capturable in a HIP graph); the partition reads the device lengths
+ * inside the kernel.  With one split no workspace is needed and the output is written directly.
  */
 fp8attn_status fp8attn_decode_paged(const fp8attn_attn_args* args, int32_t num_splits,
                                     void* workspace, size_t workspace_bytes,

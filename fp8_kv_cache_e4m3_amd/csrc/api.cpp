@@ -61,11 +61,11 @@ int cu_count() {
 }
 
 // Supported (q dtype, head dim) pairs: native FP8 at head dim 256 (vLLM PR #63139, Overview) and
-// BF16 Q at head dim 512 (vLLM PR #60372, Overview), plus head dims 64, 128 and 192 for both
-// (vLLM PR #63139, Overview: the FA4 native FP8 forward also covers 64/96/128/192; 96 is not a
-// multiple of the 64-wide FP8 MFMA k-step and is not built).
+// BF16 Q at head dim 512 (vLLM PR #60372, Overview), plus head dims 64, 96, 128 and 192 for both
+// (vLLM PR #63139, Overview: the FA4 native FP8 forward also covers 64/96/128/192).  96 is not a
+// multiple of the 64-byte k-step: decode runs it in a 128 layout, FP8 prefill on the decode kernel.
 bool supported_combo(int32_t q_dtype, int32_t d) {
-  const bool small = d == 64 || d == 128 || d == 192;
+  const bool small = d == 64 || d == 96 || d == 128 || d == 192;
   if (q_dtype == FP8ATTN_E4M3 || q_dtype == FP8ATTN_BF16_TO_E4M3) return small || d == 256;
   if (q_dtype == FP8ATTN_BF16) return small || d == 512;
   return false;
@@ -86,8 +86,8 @@ fp8attn_status validate_attn(const char* fn, const fp8attn_attn_args* a, bool de
   if (!supported_combo(a->q_dtype, a->head_dim))
     return fail(FP8ATTN_ERR_UNSUPPORTED,
                 "%s: unsupported combination q=%s k=e4m3 v=e4m3 head_size=%d head_size_v=%d "
-                "(supported: q=e4m3 or bf16->e4m3 with head_size 64, 128, 192 or 256; q=bf16 with head_size 64, 128, "
-                "192 or 512; "
+                "(supported: q=e4m3 or bf16->e4m3 with head_size 64, 96, 128, 192 or 256; q=bf16 with head_size 64, "
+                "96, 128, 192 or 512; "
                 "k/v always e4m3 with head_size_v == head_size)",
                 fn, dtype_name(a->q_dtype), a->head_dim, a->head_dim);
   if (a->causal != 1)
@@ -410,10 +410,11 @@ fp8attn_status fp8attn_prefill_varlen(const fp8attn_attn_args* args, hipStream_t
   if (args->total_q == 0 || args->batch == 0) return ok();
   fp8attn::AttnParams p = make_params(args);
   hipError_t e;
-  if (args->q_dtype == FP8ATTN_E4M3 || args->q_dtype == FP8ATTN_BF16_TO_E4M3) {
+  if ((args->q_dtype == FP8ATTN_E4M3 || args->q_dtype == FP8ATTN_BF16_TO_E4M3) && args->head_dim != 96) {
     e = fp8attn::launch_prefill_fp8(p, args->head_dim, args->q_dtype == FP8ATTN_BF16_TO_E4M3, stream);
   } else {
-    // BF16 queries: the split-KV kernel over 16-row query tiles, one split per tile.
+    // BF16 queries, and head dim 96 (whose rows do not split into the prefill tiles' 64-byte
+    // k-steps): the split-KV kernel over 16-row query tiles, one split per tile.
     const int G = args->num_q_heads / args->num_kv_heads;
     p.row_groups = (args->max_seqlen_q * G + 15) / 16;
     p.num_splits = 1;
@@ -421,7 +422,7 @@ fp8attn_status fp8attn_prefill_varlen(const fp8attn_attn_args* args, hipStream_t
     const int64_t grid = (int64_t)args->num_kv_heads * args->batch * p.row_groups;
     if (grid >= (int64_t)1 << 31)
       return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: grid of %lld blocks is too large", fn, (long long)grid);
-    e = fp8attn::launch_decode(p, fp8attn::kQBf16, args->head_dim, grid, stream);
+    e = fp8attn::launch_decode(p, args->q_dtype, args->head_dim, grid, stream);
   }
   if (e != hipSuccess) return hip_fail(fn, e);
   return ok();
@@ -434,8 +435,8 @@ fp8attn_status fp8attn_splitkv_combine(const float* partial_o, const float* part
   const char* fn = "fp8attn_splitkv_combine";
   if (num_splits <= 0 || total_q < 0 || num_q_heads <= 0)
     return fail(FP8ATTN_ERR_INVALID_ARG, "%s: num_splits > 0, total_q >= 0 and num_q_heads > 0 required", fn);
-  if (head_dim != 64 && head_dim != 128 && head_dim != 192 && head_dim != 256 && head_dim != 512)
-    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128, 192, 256, 512}", fn, head_dim);
+  if (head_dim != 64 && head_dim != 96 && head_dim != 128 && head_dim != 192 && head_dim != 256 && head_dim != 512)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 96, 128, 192, 256, 512}", fn, head_dim);
   if (out_stride_tok < 0 || out_stride_head < 0)
     return fail(FP8ATTN_ERR_INVALID_ARG, "%s: output strides must be >= 0", fn);
   if (total_q == 0) return ok();

@@ -1,7 +1,7 @@
 // Log-sum-exp combine of split-KV partials (vLLM PR #60372, Details: the combine work that
 // split-KV adds).  One wave per row (token, q head): M = max_s lse_s, w_s = exp(lse_s - M),
 // o = sum_s w_s o_s / sum_s w_s, lse = M + ln sum_s w_s.  Splits with lse = -inf are skipped
-// (their partials are never read).  Each lane owns D/64 contiguous values of the row.
+// (their partials are never read).  Each lane owns ceil(D/64) contiguous values of the row.
 #include "device.h"
 #include "params.h"
 
@@ -13,10 +13,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
                                                       int64_t rows, int32_t hq, __bf16* __restrict__ out,
                                                       int64_t out_stride_tok, int64_t out_stride_head,
                                                       float* __restrict__ lse_out) {
-  constexpr int PL = D / 64;  // values per lane
+  constexpr int PL = (D + 63) / 64;  // values per lane (head dim 96: lanes 48.. hold none)
   const int lane = threadIdx.x & 63;
   const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= rows) return;
+  const bool lane_ok = lane * PL < D;
   float M = kNegInf;
   for (int s = 0; s < S; ++s) M = fmaxf(M, part_lse[(int64_t)s * rows + n]);
   float acc[PL];
@@ -39,7 +40,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
         const f32x4_t a = *reinterpret_cast<const f32x4_t*>(src);
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c] += w * a[c];
-      } else {
+      } else if (lane_ok) {
 #pragma unroll
         for (int c = 0; c < PL; ++c) acc[c] += w * src[c];
       }
@@ -48,8 +49,10 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
   const int64_t tok = n / hq, hh = n % hq;
   __bf16* dst = out + tok * out_stride_tok + hh * out_stride_head + lane * PL;
+  if (lane_ok) {
 #pragma unroll
-  for (int c = 0; c < PL; ++c) dst[c] = (__bf16)(acc[c] * inv);
+    for (int c = 0; c < PL; ++c) dst[c] = (__bf16)(acc[c] * inv);
+  }
   if (lse_out && lane == 0) lse_out[n] = wsum > 0.f ? M + __logf(wsum) : kNegInf;
 }
 
@@ -66,10 +69,11 @@ __global__ void __launch_bounds__(256) combine_parts_kernel(const float* __restr
                                                             __bf16* __restrict__ out,
                                                             int64_t out_stride_tok, int64_t out_stride_head,
                                                             float* __restrict__ lse_out, int32_t hq) {
-  constexpr int PL = D / 64;  // values per lane
+  constexpr int PL = (D + 63) / 64;  // values per lane (head dim 96: lanes 48.. hold none)
   const int lane = threadIdx.x & 63;
   const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= n_rows) return;
+  const bool lane_ok = lane * PL < D;
   const int g = (int)(n >> 4), r = (int)(n & 15);
   const int h = g / tiles_per_head, j = g - h * tiles_per_head;
   const int b = j / row_groups, rt = j - b * row_groups;
@@ -94,15 +98,19 @@ __global__ void __launch_bounds__(256) combine_parts_kernel(const float* __restr
       const float w = __expf(l - M);
       wsum += w;
       const float* src = part_o + e * D + lane * PL;
+      if (lane_ok) {
 #pragma unroll
-      for (int c = 0; c < PL; ++c) acc[c] += w * src[c];
+        for (int c = 0; c < PL; ++c) acc[c] += w * src[c];
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
   const int64_t tok = t0 + row / group, hh = (int64_t)h * group + row % group;
   __bf16* dst = out + tok * out_stride_tok + hh * out_stride_head + lane * PL;
+  if (lane_ok) {
 #pragma unroll
-  for (int c = 0; c < PL; ++c) dst[c] = (__bf16)(acc[c] * inv);
+    for (int c = 0; c < PL; ++c) dst[c] = (__bf16)(acc[c] * inv);
+  }
   if (lse_out && lane == 0) lse_out[tok * hq + hh] = wsum > 0.f ? M + __logf(wsum) : kNegInf;
 }
 
@@ -124,6 +132,7 @@ hipError_t launch_combine_parts(const float* part_o, const float* part_lse, cons
     case 256: FP8ATTN_COMBINE_PARTS(256); break;
     case 192: FP8ATTN_COMBINE_PARTS(192); break;
     case 128: FP8ATTN_COMBINE_PARTS(128); break;
+    case 96: FP8ATTN_COMBINE_PARTS(96); break;
     default: FP8ATTN_COMBINE_PARTS(64); break;
   }
 #undef FP8ATTN_COMBINE_PARTS
@@ -148,6 +157,9 @@ hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t S,
                        out_stride_tok, out_stride_head, lse_out);
   else if (d == 128)
     hipLaunchKernelGGL(combine_kernel<128>, g, blk, 0, stream, part_o, part_lse, S, rows, hq, o,
+                       out_stride_tok, out_stride_head, lse_out);
+  else if (d == 96)
+    hipLaunchKernelGGL(combine_kernel<96>, g, blk, 0, stream, part_o, part_lse, S, rows, hq, o,
                        out_stride_tok, out_stride_head, lse_out);
   else
     hipLaunchKernelGGL(combine_kernel<64>, g, blk, 0, stream, part_o, part_lse, S, rows, hq, o,

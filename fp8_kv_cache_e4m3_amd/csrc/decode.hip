@@ -64,17 +64,30 @@ struct UnitOffsets {
   uint32_t v[4];
 };
 
-template <int D, bool NT>
+// D: the register layout's head dim; DV < D (head dim 96 in a 128 layout): the lanes whose
+// bytes lie past DV (k_hi_ok false: the last K chunk; v_ok false: the V columns) load nothing
+// and hold zeros, so no byte outside the head is read and the padding adds nothing.
+template <int D, int DV, bool NT>
 __device__ __forceinline__ void load_unit(UnitRegs<D>& ur, const uint8_t* __restrict__ kunit,
-                                          const uint8_t* __restrict__ vunit, const UnitOffsets& off) {
+                                          const uint8_t* __restrict__ vunit, const UnitOffsets& off,
+                                          const bool k_hi_ok, const bool v_ok) {
   using S = DecodeShape<D>;
 #pragma unroll
-  for (int c = 0; c < S::KCH; ++c)
-    ur.k[c] = stream_load<NT>(reinterpret_cast<const u32x4_t*>(kunit + off.k + 64 * c));
+  for (int c = 0; c < S::KCH; ++c) {
+    if (DV == D || c < S::KCH - 1 || k_hi_ok)
+      ur.k[c] = stream_load<NT>(reinterpret_cast<const u32x4_t*>(kunit + off.k + 64 * c));
+    else
+      ur.k[c] = u32x4_t{0, 0, 0, 0};
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int blk = 0; blk < S::VBLK; ++blk) {
+      if (DV != D && !v_ok) {
+#pragma unroll
+        for (int x = 0; x < S::CW / 4; ++x) ur.v[i][blk][x] = 0u;
+        continue;
+      }
       const uint8_t* vp = vunit + off.v[i] + blk * 16 * S::CW;
       if constexpr (S::CW == 16) {
         const u32x4_t w = stream_load<NT>(reinterpret_cast<const u32x4_t*>(vp));
@@ -124,8 +137,10 @@ template <int QM, int D, bool BAL>
 __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, const int h, const int rt,
                                             const int o0, const int o1, const int pidx, const bool whole) {
   constexpr bool QFP8 = QM != kQBf16;   // QK^T on the FP8 MFMA
-  using S = DecodeShape<D>;
-  using T = DecodeTune<QFP8, D>;
+  // head dim 96 runs in the 128 layout: the bytes past 96 are never loaded and count as zeros
+  constexpr int DP = D == 96 ? 128 : D;
+  using S = DecodeShape<DP>;
+  using T = DecodeTune<QFP8, DP>;
   constexpr int NBUF = T::NBUF;
   // LDS: the 4 waves' softmax state and O tiles for the final merge
   __shared__ __attribute__((aligned(16))) float sm_o[4][16][S::RS];
@@ -196,14 +211,15 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
   int pg_vec = bt[min(pg_base + lane, pg_last)];
 
   // ---- Q^T operand (rows on lane columns) ---------------------------------------------------
-  QRegs<QFP8, D> qr;
+  QRegs<QFP8, DP> qr;
   u32x4_t qraw[QM == kQBf16E4M3 ? 2 * S::KCH : 1];
   if constexpr (QM == kQE4M3) {
     const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)(t0 + tok) * p.q_stride_tok +
                         (int64_t)hq * p.q_stride_head + 16 * grp;
 #pragma unroll
     for (int c = 0; c < S::KCH; ++c) {
-      u32x4_t w = rvalid ? *reinterpret_cast<const u32x4_t*>(qp + 64 * c) : u32x4_t{0, 0, 0, 0};
+      const bool ok = rvalid && (D == DP || 64 * c + 16 * grp < D);
+      u32x4_t w = ok ? *reinterpret_cast<const u32x4_t*>(qp + 64 * c) : u32x4_t{0, 0, 0, 0};
       qr.q[2 * c] = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
       qr.q[2 * c + 1] = (uint64_t)w[2] | ((uint64_t)w[3] << 32);
     }
@@ -214,8 +230,10 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
                        (int64_t)hq * p.q_stride_head + 16 * grp;
 #pragma unroll
     for (int c = 0; c < S::KCH; ++c) {
+      const bool ok = D == DP || 64 * c + 16 * grp < D;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) qraw[2 * c + hf] = *reinterpret_cast<const u32x4_t*>(qp + 64 * c + 8 * hf);
+      for (int hf = 0; hf < 2; ++hf)
+        qraw[2 * c + hf] = ok ? *reinterpret_cast<const u32x4_t*>(qp + 64 * c + 8 * hf) : u32x4_t{0, 0, 0, 0};
     }
   } else {
     const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)(t0 + tok) * p.q_stride_tok +
@@ -223,8 +241,9 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
 #pragma unroll
     for (int c = 0; c < S::KCH; ++c) {
       const bf16x8_t z = {};
-      qr.q[2 * c] = rvalid ? *reinterpret_cast<const bf16x8_t*>(qp + 64 * c) : z;
-      qr.q[2 * c + 1] = rvalid ? *reinterpret_cast<const bf16x8_t*>(qp + 64 * c + 8) : z;
+      const bool ok = rvalid && (D == DP || 64 * c + 16 * grp < D);
+      qr.q[2 * c] = ok ? *reinterpret_cast<const bf16x8_t*>(qp + 64 * c) : z;
+      qr.q[2 * c + 1] = ok ? *reinterpret_cast<const bf16x8_t*>(qp + 64 * c + 8) : z;
     }
   }
   f32x4_t oacc[S::NT];
@@ -245,6 +264,9 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
     return __builtin_amdgcn_readlane(pg_vec, pi - pg_base);
   };
 
+  // (head dim 96 in the 128 layout: this lane's last K chunk, and its V columns, lie in the head)
+  const bool k_hi_ok = 64 * (S::KCH - 1) + 16 * grp < D;
+  const bool v_ok = col * S::CW < D;
   UnitOffsets uoff;
   uoff.k = (uint32_t)(col * sT) + 16u * (uint32_t)grp;
 #pragma unroll
@@ -253,7 +275,7 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
   // compiler waits for exactly the oldest unit.  They read the last unit's first 16 bytes in every
   // lane: one cache line, which costs next to nothing and lands quickly at the end of the stream.
   const int ulast = su1 - 1;
-  auto issue = [&](UnitRegs<D>& ur, int u) __attribute__((always_inline)) {
+  auto issue = [&](UnitRegs<DP>& ur, int u) __attribute__((always_inline)) {
     const bool trailing = u > ulast;
     const int uc = trailing ? ulast : u;
     const int64_t unit = page_of(uc) * sP + (int64_t)((uc * 16) % ps) * sT;
@@ -261,7 +283,7 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
     o.k = trailing ? 0u : o.k;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o.v[i] = trailing ? 0u : o.v[i];
-    load_unit<D, T::NT>(ur, kbase + unit, vbase + unit, o);
+    load_unit<DP, D, T::NT>(ur, kbase + unit, vbase + unit, o, k_hi_ok, v_ok);
   };
 
   // S^T tile of a unit: rows = its 16 keys, columns = the 16 query rows
@@ -323,7 +345,7 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
   // O^T += V^T * P^T with V in registers (lane (col, g) holds bytes col*CW.. of keys 4g..4g+3):
   // a 4x4 byte transpose gives, per O^T tile t, row col <-> d = 16 col + t (d256) or the
   // analogous interleave (d64, d512)
-  auto compute = [&](const UnitRegs<D>& ur, int u) __attribute__((always_inline)) {
+  auto compute = [&](const UnitRegs<DP>& ur, int u) __attribute__((always_inline)) {
     const bf16x4_t pb = softmax(qk(ur.k), u);
 #pragma unroll
     for (int blk = 0; blk < S::VBLK; ++blk) {
@@ -347,7 +369,7 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
     // A ring of NBUF register buffers: NBUF - 1 units stay in flight while one is computed.
     // Every trip issues the same loads (see issue), so the compiler can wait for exactly the
     // oldest unit instead of draining every outstanding load.
-    UnitRegs<D> buf[NBUF];
+    UnitRegs<DP> buf[NBUF];
 #pragma unroll
     for (int k = 0; k < NBUF; ++k) issue(buf[k], u0 + 4 * k);
     if constexpr (QM == kQBf16E4M3) {
@@ -398,10 +420,10 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
   // ---- final: thread -> (row, d-part) -------------------------------------------------------
   {
     const int row = threadIdx.x & 15;
-    const int part = threadIdx.x >> 4;                 // 16 parts of D/16 values
-    constexpr int PW = D / 16;
+    const int part = threadIdx.x >> 4;                 // 16 parts of DP/16 values
+    constexpr int PW = DP / 16;
     const int rr = row0 + row;
-    if (rr < nrows) {
+    if (rr < nrows && part * PW < D) {                 // (parts past a padded head dim write nothing)
       float mw[4], M = kNegInf;
 #pragma unroll
       for (int w = 0; w < 4; ++w) { mw[w] = sm_m[w][row]; M = fmaxf(M, mw[w]); }
@@ -578,6 +600,7 @@ static void launch_decode_dims(const AttnParams& p, int head_dim, dim3 g, hipStr
   } while (0)
   switch (head_dim) {
     case 64: FP8ATTN_DECODE(64); break;
+    case 96: FP8ATTN_DECODE(96); break;
     case 128: FP8ATTN_DECODE(128); break;
     case 192: FP8ATTN_DECODE(192); break;
     default:

@@ -130,9 +130,9 @@ fp8attn_status fp8attn_quantize_q(const void* q_bf16, int64_t num_tokens, int32_
 
 /*
  * Paged attention for varlen batches of new tokens (prefill / chunked prefill), any q_len.
- * Supported: (q_dtype E4M3 or BF16_TO_E4M3, head_dim 64, 128, 192 or 256) and (q_dtype BF16,
- * head_dim 64, 128, 192 or 512); K/V are E4M3 with V head dim equal to head_dim ([60372] review
- * thread; [63139] Overview lists 64/96/128/192/256 for the native FP8 forward, 96 is not built).
+ * Supported: (q_dtype E4M3 or BF16_TO_E4M3, head_dim 64, 96, 128, 192 or 256) and (q_dtype
+ * BF16, head_dim 64, 96, 128, 192 or 512); K/V are E4M3 with V head dim equal to head_dim
+ * ([60372] review thread; [63139] Overview lists 64/96/128/192/256 for the native FP8 forward).
  * Writes args->out and, if non-NULL, args->lse.
  */
 fp8attn_status fp8attn_prefill_varlen(const fp8attn_attn_args* args, hipStream_t stream);
@@ -170,7 +170,7 @@ fp8attn_status fp8attn_decode_paged(const fp8attn_attn_args* args, int32_t num_s
  *   partial_lse : fp32 [num_splits, total_q, num_q_heads] contiguous (natural log)
  *   out_bf16    : bf16 [total_q, num_q_heads, head_dim] with the given element strides
  *   lse_out     : optional fp32 [total_q, num_q_heads] contiguous
- * head_dim must be 64, 128, 192, 256 or 512.  A row whose every split is -inf gets out = 0,
+ * head_dim must be 64, 96, 128, 192, 256 or 512.  A row whose every split is -inf gets out = 0,
  * lse = -inf.
  */
 fp8attn_status fp8attn_splitkv_combine(const float* partial_o, const float* partial_lse,

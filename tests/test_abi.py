@@ -76,8 +76,8 @@ def _status(a, fn="prefill"):
     ({"head_dim": 256}, fa.ERR_UNSUPPORTED, ["q=bf16", "k=e4m3", "v=e4m3", "head_size=256", "head_size_v=256"]),
     ({"q_dtype": fa.E4M3, "head_dim": 512}, fa.ERR_UNSUPPORTED, ["q=e4m3", "head_size=512"]),
     ({"q_dtype": fa.BF16_TO_E4M3, "head_dim": 512}, fa.ERR_UNSUPPORTED, ["q=bf16->e4m3", "head_size=512"]),
-    ({"head_dim": 96}, fa.ERR_UNSUPPORTED, ["head_size=96"]),
-    ({"q_dtype": fa.E4M3, "head_dim": 96}, fa.ERR_UNSUPPORTED, ["q=e4m3", "head_size=96"]),
+    ({"head_dim": 80}, fa.ERR_UNSUPPORTED, ["head_size=80"]),
+    ({"q_dtype": fa.E4M3, "head_dim": 80}, fa.ERR_UNSUPPORTED, ["q=e4m3", "head_size=80"]),
     ({"page_size": 32}, fa.ERR_UNSUPPORTED, ["page_size 32", "multiple of 64"]),
     ({"page_size": 96}, fa.ERR_UNSUPPORTED, ["page_size 96"]),
     ({"window": 0}, fa.ERR_INVALID_ARG, ["window"]),
@@ -106,7 +106,7 @@ def test_rejections(fn, change, status, words):
 
 @pytest.mark.parametrize("fn", ["prefill", "decode"])
 @pytest.mark.parametrize("q_dtype", [fa.E4M3, fa.BF16_TO_E4M3])
-@pytest.mark.parametrize("head_dim", [64, 128, 192, 256])
+@pytest.mark.parametrize("head_dim", [64, 96, 128, 192, 256])
 def test_quantized_q_modes_pass_validation(fn, q_dtype, head_dim):
     # Both quantized-query modes are accepted at head_size 64 and 256, with or without a
     # q_descale; an empty batch then returns OK without touching the device.
@@ -143,8 +143,8 @@ def test_quantize_rejections():
 def test_combine_rejections():
     L = fa.LIB
     assert L.fp8attn_splitkv_combine(None, None, 0, 1, 1, 64, None, 64, 64, None, None) == fa.ERR_INVALID_ARG
-    assert L.fp8attn_splitkv_combine(None, None, 2, 1, 1, 96, None, 64, 64, None, None) == fa.ERR_UNSUPPORTED
-    assert "head_dim 96" in fa.fp8attn_last_error()
+    assert L.fp8attn_splitkv_combine(None, None, 2, 1, 1, 80, None, 64, 64, None, None) == fa.ERR_UNSUPPORTED
+    assert "head_dim 80" in fa.fp8attn_last_error()
     assert L.fp8attn_splitkv_combine(None, None, 2, 0, 1, 64, None, 64, 64, None, None) == fa.OK
     assert L.fp8attn_splitkv_combine(None, None, 2, 3, 1, 64, None, 64, 64, None, None) == fa.ERR_INVALID_ARG
 

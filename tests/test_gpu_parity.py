@@ -220,7 +220,7 @@ def test_combine_entry_point():
 # gather: bit-exact (one-hot logits), page permutation invariance, determinism
 # ------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("q_dtype,d", [("bf16", 512), ("e4m3", 256), ("bf16", 64), ("e4m3", 64),
-                                       ("e4m3", 192), ("bf16", 128)])
+                                       ("e4m3", 192), ("bf16", 128), ("e4m3", 96), ("bf16", 96)])
 def test_one_hot_gather_bit_exact(q_dtype, d):
     """Q equal to one key's row with a huge softmax scale: every other weight is exactly 0 in
     fp32, so O must equal that key's dequantized V row bit for bit (v_descale a power of two)."""
@@ -283,15 +283,15 @@ def test_edge_cases(q_dtype, d, hq, hkv, window, seqlens, qlens, entry):
 
 
 # ------------------------------------------------------------------------------------------
-# head dims 128 and 192, both variants, both entry points; the in-kernel Q quantization gives
-# the two-call path's outputs bit for bit
+# head dims 96, 128 and 192, both variants, both entry points (96 also through the balanced
+# partition); the in-kernel Q quantization gives the two-call path's outputs bit for bit
 # ------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("d", [128, 192])
+@pytest.mark.parametrize("d", [96, 128, 192])
 @pytest.mark.parametrize("q_dtype,entry,splits", [
-    ("e4m3", "decode", 0), ("e4m3", "decode", 3), ("e4m3", "prefill", 0),
-    ("bf16", "decode", 0), ("bf16", "decode", 2), ("bf16", "prefill", 0),
+    ("e4m3", "decode", 0), ("e4m3", "decode", 3), ("e4m3", "prefill", 0), ("e4m3", "decode", -6),
+    ("bf16", "decode", 0), ("bf16", "decode", 2), ("bf16", "prefill", 0), ("bf16", "decode", -6),
 ])
-def test_head_dims_128_192(d, q_dtype, entry, splits):
+def test_head_dims(d, q_dtype, entry, splits):
     window = 300 if q_dtype == "e4m3" else -1
     if entry == "decode":     # GQA 8:1, q_len 1..16, ragged lengths
         w = wl.custom(q_dtype, d, 16, 2, window, [700, 65, 1500], [4, 16, 1], seed=d + 1)

@@ -102,7 +102,7 @@ class Runner:
     """One input set.  For E4M3 workloads the step takes bf16 Q: by default the attention call
     quantizes it in-kernel (one launch); with fused=False a separate quantize call writes the
     codes first (two launches)."""
-    def __init__(self, w, entry, fused=True):
+    def __init__(self, w, entry, fused=True, split=False):
         import torch
         import fp8_kv_cache_e4m3_amd as fa
         self.fa, self.torch, self.w, self.entry = fa, torch, w, entry
@@ -116,7 +116,7 @@ class Runner:
                                  w.max_seqlen_q, w.max_seqlen_k,
                                  w.q_descale if w.q_dtype == "e4m3" else None, w.k_descale, w.v_descale,
                                  0.0, w.window, True, self.out, self.lse,
-                                 quantize_q=(w.q_dtype == "e4m3" and fused))
+                                 quantize_q=(w.q_dtype == "e4m3" and fused), split_q=split)
         self.ws = None
         self.splits = 1
         if entry == "decode":
@@ -144,11 +144,12 @@ class Runner:
         assert st == 0, fa.fp8attn_last_error()
 
 
-def time_workload(make, entry, nsets, steps, warmup, label, fused=True):
-    """Returns dict with ms_per_step (whole step) and kernel_ms (attention call only, HIP events)."""
+def time_workload(make, entry, nsets, steps, warmup, label, fused=True, split=False):
+    """Returns dict with ms_per_step (whole step) and kernel_ms (attention call only, HIP events).
+    split: bf16 Q runs on the FP8 MFMA as two E4M3 terms (q_dtype BF16_SPLIT)."""
     import torch
     t0 = time.time()
-    runners = [Runner(make(seed), entry, fused) for seed in range(nsets)]
+    runners = [Runner(make(seed), entry, fused, split) for seed in range(nsets)]
     torch.cuda.synchronize()
     log(f"[bench] {label}: {nsets} input sets ready in {time.time() - t0:.1f}s; splits={runners[0].splits}")
     stream = torch.cuda.current_stream()
@@ -401,12 +402,15 @@ def main():
     extra = {}
     if not args.no_extra:
         specs = [
-            ("full_decode", lambda s: wl.full_decode(device="cuda", seed=200 + s), "decode", 4, "hbm"),
-            ("spec_verify", lambda s: wl.spec_verify(device="cuda", seed=300 + s), "decode", 2, "hbm"),
-            ("swa_prefill", lambda s: wl.swa_prefill(device="cuda", seed=400 + s), "prefill", 2, "mfma"),
+            ("full_decode", lambda s: wl.full_decode(device="cuda", seed=200 + s), "decode", 4, "hbm", False),
+            ("spec_verify", lambda s: wl.spec_verify(device="cuda", seed=300 + s), "decode", 2, "hbm", False),
+            ("swa_prefill", lambda s: wl.swa_prefill(device="cuda", seed=400 + s), "prefill", 2, "mfma", False),
+            # the same bf16-Q workloads with QK^T on the FP8 MFMA (split Q)
+            ("full_decode_split_q", lambda s: wl.full_decode(device="cuda", seed=200 + s), "decode", 4, "hbm", True),
+            ("spec_verify_split_q", lambda s: wl.spec_verify(device="cuda", seed=300 + s), "decode", 2, "hbm", True),
         ]
-        for name, make, entry, ns, bound in specs:
-            r = time_workload(make, entry, ns, max(5, args.steps // 5), 2, name, fused)
+        for name, make, entry, ns, bound, split in specs:
+            r = time_workload(make, entry, ns, max(5, args.steps // 5), 2, name, fused, split)
             ww = r["w"]
             tb, kvb = algo_bytes(ww, fused)
             fl = algo_flops(ww)
@@ -416,8 +420,8 @@ def main():
                  "TFLOPs": round(fl / (r["kernel_ms"] * 1e-3) / 1e12, 2)}
             # HBM bytes of the step's kernels (decode plus the partition's combine; both prefill instances)
             keys = {"full_decode": ["decode_full", "decode_full_combine"], "spec_verify": ["decode_spec"],
-                    "swa_prefill": ["prefill_swa", "prefill_swa_splitp"]}[name]
-            tr = [load_traffic(k) for k in keys]
+                    "swa_prefill": ["prefill_swa", "prefill_swa_splitp"]}.get(name)
+            tr = [load_traffic(k) for k in keys] if keys else [None]
             e["traffic"] = sum(tr) if fused and all(t is not None for t in tr) else None
             if bound == "hbm":
                 e["hbm_frac"] = round(e["kv_read_GBps"] / HBM_PEAK_GBS, 4)

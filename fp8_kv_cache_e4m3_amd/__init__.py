@@ -23,7 +23,7 @@ if not os.path.exists(_LIB_PATH):
 _lib = ctypes.CDLL(_LIB_PATH)
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-BF16, E4M3, BF16_TO_E4M3 = 0, 1, 2
+BF16, E4M3, BF16_TO_E4M3, BF16_SPLIT = 0, 1, 2, 3
 _STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}
 
 
@@ -160,13 +160,15 @@ def fp8attn_quantize_q(q: torch.Tensor, q_descale=None, out=None, stream=None) -
 def make_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seqlen_k,
               q_descale=None, k_descale=None, v_descale=None, softmax_scale=0.0, window=-1, causal=True,
               out=None, lse=None, descale_strides=(0, 0), total_q=None, batch=None,
-              quantize_q=False) -> AttnArgs:
+              quantize_q=False, split_q=False) -> AttnArgs:
     """Fill the C argument struct from tensors (shapes: q [T, Hq, d]; caches [pages, page, Hkv, d]).
-    quantize_q: bf16 q is quantized to E4M3 inside the call (q_dtype BF16_TO_E4M3)."""
+    quantize_q: bf16 q is quantized to E4M3 inside the call (q_dtype BF16_TO_E4M3).
+    split_q: bf16 q is split into two E4M3 terms inside the call (q_dtype BF16_SPLIT)."""
     k_cache, v_cache = _bytes(k_cache), _bytes(v_cache)
     a = AttnArgs()
     if q.dtype == torch.bfloat16:
-        a.q_dtype = BF16_TO_E4M3 if quantize_q else BF16
+        assert not (quantize_q and split_q), "quantize_q and split_q exclude each other"
+        a.q_dtype = BF16_TO_E4M3 if quantize_q else BF16_SPLIT if split_q else BF16
     else:
         q = _bytes(q)
         assert q.dtype == torch.uint8, "q must be bf16 or E4M3 codes"
@@ -210,11 +212,11 @@ def _alloc_out(q, out, lse, want_lse):
 def fp8attn_prefill_varlen(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, max_seqlen_q,
                            max_seqlen_k, q_descale=None, k_descale=None, v_descale=None, softmax_scale=0.0,
                            window=-1, causal=True, out=None, lse=None, want_lse=True, descale_strides=(0, 0),
-                           quantize_q=False, stream=None):
+                           quantize_q=False, split_q=False, stream=None):
     out, lse = _alloc_out(q, out, lse, want_lse)
     a = make_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seqlen_k,
                   q_descale, k_descale, v_descale, softmax_scale, window, causal, out, lse, descale_strides,
-                  quantize_q=quantize_q)
+                  quantize_q=quantize_q, split_q=split_q)
     _check("fp8attn_prefill_varlen", _lib.fp8attn_prefill_varlen(ctypes.byref(a), _stream(stream)))
     return out, lse
 
@@ -231,15 +233,15 @@ def decode_workspace_size(args: AttnArgs, num_splits: int = 0):
 def fp8attn_decode_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seqlen_k,
                          q_descale=None, k_descale=None, v_descale=None, softmax_scale=0.0, window=-1,
                          causal=True, out=None, lse=None, want_lse=True, num_splits=0, workspace=None,
-                         descale_strides=(0, 0), quantize_q=False, stream=None):
+                         descale_strides=(0, 0), quantize_q=False, split_q=False, stream=None):
     """Returns (out, lse, splits_used).  num_splits: 0 automatic, N > 0 that many splits, -R the
     balanced partition into R parts (splits_used is then -R).  The workspace is sized by a query
     and allocated with torch if the caller passes none.  quantize_q: bf16 q is quantized to E4M3
-    inside the call."""
+    inside the call; split_q: bf16 q runs on the FP8 MFMA as two E4M3 terms (q_dtype BF16_SPLIT)."""
     out, lse = _alloc_out(q, out, lse, want_lse)
     a = make_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seqlen_k,
                   q_descale, k_descale, v_descale, softmax_scale, window, causal, out, lse, descale_strides,
-                  quantize_q=quantize_q)
+                  quantize_q=quantize_q, split_q=split_q)
     need, used = decode_workspace_size(a, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

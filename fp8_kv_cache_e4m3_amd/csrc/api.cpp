@@ -41,7 +41,8 @@ fp8attn_status hip_fail(const char* where, hipError_t e) {
 }
 
 const char* dtype_name(int32_t t) {
-  return t == FP8ATTN_BF16 ? "bf16" : t == FP8ATTN_E4M3 ? "e4m3" : t == FP8ATTN_BF16_TO_E4M3 ? "bf16->e4m3" : "unknown";
+  return t == FP8ATTN_BF16 ? "bf16" : t == FP8ATTN_E4M3 ? "e4m3" : t == FP8ATTN_BF16_TO_E4M3 ? "bf16->e4m3"
+         : t == FP8ATTN_BF16_SPLIT ? "bf16-split" : "unknown";
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -62,18 +63,20 @@ int cu_count() {
 
 // Supported (q dtype, head dim) pairs: native FP8 at head dim 256 (vLLM PR #63139, Overview) and
 // BF16 Q at head dim 512 (vLLM PR #60372, Overview), plus head dims 64, 96, 128 and 192 for both
-// (vLLM PR #63139, Overview: the FA4 native FP8 forward also covers 64/96/128/192).  96 is not a
-// multiple of the 64-byte k-step: decode runs it in a 128 layout, FP8 prefill on the decode kernel.
+// (vLLM PR #63139, Overview: the FA4 native FP8 forward also covers 64/96/128/192), and 256 for
+// BF16 Q (same kernel).  96 is not a multiple of the 64-byte k-step: decode runs it in a 128
+// layout, FP8 prefill on the decode kernel.
 bool supported_combo(int32_t q_dtype, int32_t d) {
   const bool small = d == 64 || d == 96 || d == 128 || d == 192;
   if (q_dtype == FP8ATTN_E4M3 || q_dtype == FP8ATTN_BF16_TO_E4M3) return small || d == 256;
-  if (q_dtype == FP8ATTN_BF16) return small || d == 512;
+  if (q_dtype == FP8ATTN_BF16 || q_dtype == FP8ATTN_BF16_SPLIT) return small || d == 256 || d == 512;
   return false;
 }
 
 fp8attn_status validate_attn(const char* fn, const fp8attn_attn_args* a, bool decode) {
   if (!a) return fail(FP8ATTN_ERR_INVALID_ARG, "%s: args is NULL", fn);
-  if (a->q_dtype != FP8ATTN_BF16 && a->q_dtype != FP8ATTN_E4M3 && a->q_dtype != FP8ATTN_BF16_TO_E4M3)
+  if (a->q_dtype != FP8ATTN_BF16 && a->q_dtype != FP8ATTN_E4M3 && a->q_dtype != FP8ATTN_BF16_TO_E4M3 &&
+      a->q_dtype != FP8ATTN_BF16_SPLIT)
     return fail(FP8ATTN_ERR_INVALID_ARG, "%s: unknown q_dtype %d", fn, a->q_dtype);
   if (a->reserved0 != 0 || a->reserved1 != 0)
     return fail(FP8ATTN_ERR_INVALID_ARG, "%s: reserved fields must be 0", fn);
@@ -86,8 +89,8 @@ fp8attn_status validate_attn(const char* fn, const fp8attn_attn_args* a, bool de
   if (!supported_combo(a->q_dtype, a->head_dim))
     return fail(FP8ATTN_ERR_UNSUPPORTED,
                 "%s: unsupported combination q=%s k=e4m3 v=e4m3 head_size=%d head_size_v=%d "
-                "(supported: q=e4m3 or bf16->e4m3 with head_size 64, 96, 128, 192 or 256; q=bf16 with head_size 64, "
-                "96, 128, 192 or 512; "
+                "(supported: q=e4m3 or bf16->e4m3 with head_size 64, 96, 128, 192 or 256; q=bf16 or bf16-split with "
+                "head_size 64, 96, 128, 192, 256 or 512; "
                 "k/v always e4m3 with head_size_v == head_size)",
                 fn, dtype_name(a->q_dtype), a->head_dim, a->head_dim);
   if (a->causal != 1)
@@ -101,10 +104,10 @@ fp8attn_status validate_attn(const char* fn, const fp8attn_attn_args* a, bool de
     return fail(FP8ATTN_ERR_UNSUPPORTED,
                 "%s: page_size %d is not a positive multiple of 64 (q=%s k=e4m3 v=e4m3 head_size=%d)", fn,
                 a->page_size, dtype_name(a->q_dtype), a->head_dim);
-  if (a->q_dtype == FP8ATTN_BF16 && a->q_descale != nullptr)
+  if ((a->q_dtype == FP8ATTN_BF16 || a->q_dtype == FP8ATTN_BF16_SPLIT) && a->q_descale != nullptr)
     return fail(FP8ATTN_ERR_UNSUPPORTED,
-                "%s: q=bf16 takes unquantized queries, so q_descale must be NULL (k=e4m3 v=e4m3 head_size=%d)",
-                fn, a->head_dim);
+                "%s: q=%s takes unquantized queries, so q_descale must be NULL (k=e4m3 v=e4m3 head_size=%d)",
+                fn, dtype_name(a->q_dtype), a->head_dim);
   if (a->batch < 0 || a->total_q < 0 || a->max_seqlen_q < 0 || a->max_seqlen_k < 0)
     return fail(FP8ATTN_ERR_INVALID_ARG, "%s: batch, total_q, max_seqlen_q and max_seqlen_k must be >= 0", fn);
   if (a->total_q > 0 && a->max_seqlen_q == 0)

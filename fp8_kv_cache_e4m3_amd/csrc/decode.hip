@@ -8,7 +8,11 @@
 //   QM = kQBf16E4M3: bf16 Q quantized to E4M3 as the kernel loads it, with the same arithmetic
 //                   as fp8attn_quantize_q (identical codes), then the same FP8 path;
 //   QM = kQBf16   : BF16 Q, K dequantized in registers (exact: E4M3 values are bf16 values),
-//                   QK^T on the BF16 MFMA.
+//                   QK^T on the BF16 MFMA;
+//   QM = kQBf16Split: BF16 Q split into two E4M3 terms per value (per-row power-of-two scale),
+//                   QK^T on the FP8 MFMA as a two-part accumulation (vLLM PR #60372, review
+//                   thread: the d512 FP8-MMA kernel keeps BF16 queries and builds a split QK
+//                   accumulation; the split itself is not described there, see split8_bf16_e4m3).
 // PV runs on the BF16 MFMA in both variants: V bytes are dequantized exactly to bf16 and P is
 // rounded once to bf16.  Decode is HBM-bound, so the cheaper FP8 PV would not move the time but
 // would cost accuracy on short rows.
@@ -122,6 +126,46 @@ struct DecodeTune {
   static constexpr int MIN_WAVES = D == 256 ? 2 : 1;
 };
 
+// Split Q (kQBf16Split): one query row, scaled by a power of two 2^e so that its largest
+// magnitude is at most 448, is written as hi + lo / 16 with hi = E4M3(x 2^e) and
+// lo = E4M3(16 (x 2^e - hi)).  A bf16 value has 8 significant bits; hi keeps the top 4 (rounded
+// to nearest even) and the residual then has at most 4, so hi + lo / 16 equals x 2^e exactly
+// unless hi or lo falls below E4M3's normal range (|x| under about 2^-14 of the row's largest).
+// QK^T is then accumulated in two parts on the FP8 MFMA, S = K hi + (K lo) / 16, and scaled back
+// by 2^-e: the BF16 product up to the order of the fp32 sums.
+__device__ __forceinline__ void split8_bf16_e4m3(const u32x4_t w, const float scale, uint64_t& hi, uint64_t& lo) {
+  float x[8], r[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(w[k] << 16) * scale;           // exact: a power-of-two scale
+    x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u) * scale;
+  }
+  int h[2], l[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    h[q] = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q], x[4 * q + 1], 0, false);
+    h[q] = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q + 2], x[4 * q + 3], h[q], true);
+    const f32x2_t d0 = __builtin_amdgcn_cvt_pk_f32_fp8(h[q], false);
+    const f32x2_t d1 = __builtin_amdgcn_cvt_pk_f32_fp8(h[q], true);
+    r[4 * q] = (x[4 * q] - d0[0]) * 16.0f;                    // exact differences
+    r[4 * q + 1] = (x[4 * q + 1] - d0[1]) * 16.0f;
+    r[4 * q + 2] = (x[4 * q + 2] - d1[0]) * 16.0f;
+    r[4 * q + 3] = (x[4 * q + 3] - d1[1]) * 16.0f;
+    l[q] = __builtin_amdgcn_cvt_pk_fp8_f32(r[4 * q], r[4 * q + 1], 0, false);
+    l[q] = __builtin_amdgcn_cvt_pk_fp8_f32(r[4 * q + 2], r[4 * q + 3], l[q], true);
+  }
+  hi = (uint64_t)(uint32_t)h[0] | ((uint64_t)(uint32_t)h[1] << 32);
+  lo = (uint64_t)(uint32_t)l[0] | ((uint64_t)(uint32_t)l[1] << 32);
+}
+
+// 2^e with e = floor(log2(448 / amax)), clamped to [-126, 126] (both 2^e and 2^-e normal); an
+// all-zero row takes 2^126.
+__device__ __forceinline__ int split_exponent(float amax) {
+  const float m = 448.0f / amax;
+  const int e = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127;
+  return max(-126, min(126, e));
+}
+
 template <bool QFP8, int D>
 struct QRegs;
 template <int D>
@@ -211,8 +255,10 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
   int pg_vec = bt[min(pg_base + lane, pg_last)];
 
   // ---- Q^T operand (rows on lane columns) ---------------------------------------------------
-  QRegs<QFP8, DP> qr;
-  u32x4_t qraw[QM == kQBf16E4M3 ? 2 * S::KCH : 1];
+  constexpr bool SPLIT = QM == kQBf16Split;
+  QRegs<QFP8, DP> qr;                                   // (split Q: the hi terms)
+  uint64_t qlo[SPLIT ? 2 * S::KCH : 1];                 // split Q: the lo terms
+  u32x4_t qraw[QM == kQBf16E4M3 || SPLIT ? 2 * S::KCH : 1];
   if constexpr (QM == kQE4M3) {
     const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)(t0 + tok) * p.q_stride_tok +
                         (int64_t)hq * p.q_stride_head + 16 * grp;
@@ -223,7 +269,7 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
       qr.q[2 * c] = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
       qr.q[2 * c + 1] = (uint64_t)w[2] | ((uint64_t)w[3] << 32);
     }
-  } else if constexpr (QM == kQBf16E4M3) {
+  } else if constexpr (QM == kQBf16E4M3 || SPLIT) {
     // the same 16 d values per k-chunk as above, read as bf16 here and quantized once the first
     // units' loads are in flight (below); a row past the end reads the clamped row
     const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)(t0 + tok) * p.q_stride_tok +
@@ -245,6 +291,25 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
       qr.q[2 * c] = ok ? *reinterpret_cast<const bf16x8_t*>(qp + 64 * c) : z;
       qr.q[2 * c + 1] = ok ? *reinterpret_cast<const bf16x8_t*>(qp + 64 * c + 8) : z;
     }
+  }
+  float cs = cscale;   // per lane for split Q: the row's 2^-e folds into the logit scale
+  if constexpr (SPLIT) {
+    // the row's largest magnitude (its 4 lane groups hold its head dim), then the split
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2 * S::KCH; ++i) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        amax = fmaxf(amax, fabsf(__uint_as_float(qraw[i][k] << 16)));
+        amax = fmaxf(amax, fabsf(__uint_as_float(qraw[i][k] & 0xffff0000u)));
+      }
+    }
+    amax = max_over_groups(amax);
+    const int e = split_exponent(amax);
+    const float up = __uint_as_float((uint32_t)(127 + e) << 23);
+    cs = cscale * __uint_as_float((uint32_t)(127 - e) << 23);
+#pragma unroll
+    for (int i = 0; i < 2 * S::KCH; ++i) split8_bf16_e4m3(qraw[i], up, qr.q[i], qlo[i]);
   }
   f32x4_t oacc[S::NT];
 #pragma unroll
@@ -289,6 +354,19 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
   // S^T tile of a unit: rows = its 16 keys, columns = the 16 query rows
   auto qk = [&](const u32x4_t (&kk)[S::KCH]) __attribute__((always_inline)) -> f32x4_t {
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (SPLIT) {   // the split accumulation: K hi + (K lo) / 16
+      f32x4_t slo = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < S::KCH; ++c) {
+        const uint64_t k0 = (uint64_t)kk[c][0] | ((uint64_t)kk[c][1] << 32);
+        const uint64_t k1 = (uint64_t)kk[c][2] | ((uint64_t)kk[c][3] << 32);
+        sacc = mfma_fp8_16x16x32(k0, qr.q[2 * c], sacc);
+        slo = mfma_fp8_16x16x32(k0, qlo[2 * c], slo);
+        sacc = mfma_fp8_16x16x32(k1, qr.q[2 * c + 1], sacc);
+        slo = mfma_fp8_16x16x32(k1, qlo[2 * c + 1], slo);
+      }
+      return sacc + slo * 0.0625f;
+    }
 #pragma unroll
     for (int c = 0; c < S::KCH; ++c) {
       if constexpr (QFP8) {
@@ -308,7 +386,7 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
   auto softmax = [&](const f32x4_t sacc, int u) __attribute__((always_inline)) -> bf16x4_t {
     float sv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = sacc[i] * cscale;
+    for (int i = 0; i < 4; ++i) sv[i] = sacc[i] * cs;
     const int j0 = u * 16;
     if (!(j0 >= full_lo && j0 + 15 <= p_first)) {
 #pragma unroll
@@ -604,9 +682,11 @@ static void launch_decode_dims(const AttnParams& p, int head_dim, dim3 g, hipStr
     case 128: FP8ATTN_DECODE(128); break;
     case 192: FP8ATTN_DECODE(192); break;
     default:
-      // the last head dim of each variant: 256 (FP8 Q) or 512 (BF16 Q)
-      if constexpr (QM == kQBf16) FP8ATTN_DECODE(512);
-      else FP8ATTN_DECODE(256);
+      // the last head dims: 256 (FP8 Q); 256 and 512 (BF16 and split Q)
+      if constexpr (QM == kQBf16 || QM == kQBf16Split) {
+        if (head_dim == 512) FP8ATTN_DECODE(512);
+        else FP8ATTN_DECODE(256);
+      } else FP8ATTN_DECODE(256);
   }
 #undef FP8ATTN_DECODE
 }
@@ -615,6 +695,7 @@ template <bool BAL>
 static void launch_decode_modes(const AttnParams& p, int q_mode, int head_dim, dim3 g, hipStream_t stream) {
   if (q_mode == kQE4M3) launch_decode_dims<kQE4M3, BAL>(p, head_dim, g, stream);
   else if (q_mode == kQBf16E4M3) launch_decode_dims<kQBf16E4M3, BAL>(p, head_dim, g, stream);
+  else if (q_mode == kQBf16Split) launch_decode_dims<kQBf16Split, BAL>(p, head_dim, g, stream);
   else launch_decode_dims<kQBf16, BAL>(p, head_dim, g, stream);
 }
 

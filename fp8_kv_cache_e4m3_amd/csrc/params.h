@@ -48,6 +48,7 @@ struct AttnParams {
 constexpr int kQBf16 = 0;       // bf16 values, BF16 MFMA with K/V dequantized
 constexpr int kQE4M3 = 1;       // E4M3 codes, FP8 MFMA
 constexpr int kQBf16E4M3 = 2;   // bf16 values quantized to E4M3 on load, FP8 MFMA
+constexpr int kQBf16Split = 3;  // bf16 values split into two E4M3 terms on load, FP8 MFMA
 
 // KV-cache write (fp8attn_cache_write)
 struct CacheWriteParams {

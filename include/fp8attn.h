@@ -58,7 +58,14 @@ typedef enum fp8attn_status {
 typedef enum fp8attn_dtype {
   FP8ATTN_BF16 = 0,              /* bfloat16 */
   FP8ATTN_E4M3 = 1,              /* OCP float8 E4M3 (torch.float8_e4m3fn), stored as bytes */
-  FP8ATTN_BF16_TO_E4M3 = 2       /* bfloat16 Q quantized to E4M3 inside the call (q only) */
+  FP8ATTN_BF16_TO_E4M3 = 2,      /* bfloat16 Q quantized to E4M3 inside the call (q only) */
+  FP8ATTN_BF16_SPLIT = 3         /* bfloat16 Q kept at full precision on the FP8 MFMA: each query
+                                    row is scaled by a power of two 2^e (largest magnitude <= 448)
+                                    and written as hi + lo/16 with hi, lo E4M3, which is exact for
+                                    every value above about 2^-14 of the row's largest; QK^T is
+                                    the two-part sum K.hi + K.lo/16, times 2^-e ([60372] review
+                                    thread: the d512 FP8-MMA kernel keeps BF16 queries and builds
+                                    a split QK accumulation).  No q_descale.  (q only) */
 } fp8attn_dtype;
 
 /*
@@ -131,8 +138,9 @@ fp8attn_status fp8attn_quantize_q(const void* q_bf16, int64_t num_tokens, int32_
 /*
  * Paged attention for varlen batches of new tokens (prefill / chunked prefill), any q_len.
  * Supported: (q_dtype E4M3 or BF16_TO_E4M3, head_dim 64, 96, 128, 192 or 256) and (q_dtype
- * BF16, head_dim 64, 96, 128, 192 or 512); K/V are E4M3 with V head dim equal to head_dim
- * ([60372] review thread; [63139] Overview lists 64/96/128/192/256 for the native FP8 forward).
+ * BF16 or BF16_SPLIT, head_dim 64, 96, 128, 192, 256 or 512); K/V are E4M3 with V head dim equal
+ * to head_dim ([60372] review thread; [63139] Overview lists 64/96/128/192/256 for the native FP8
+ * forward).
  * Writes args->out and, if non-NULL, args->lse.
  */
 fp8attn_status fp8attn_prefill_varlen(const fp8attn_attn_args* args, hipStream_t stream);

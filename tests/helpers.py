@@ -67,10 +67,11 @@ def oracle_run(w: wl.Workload, tokens=None, window=None, softmax_scale=None):
 
 
 def gpu_run(w: wl.Workload, entry="decode", num_splits=0, window=None, softmax_scale=0.0, want_lse=True,
-            out=None, q_codes=None, fused_q=False):
+            out=None, q_codes=None, fused_q=False, split_q=False):
     """Run the HIP path.  Returns (o float64 [T,Hq,d], lse [T,Hq] or None, q codes (uint8 numpy) or
     None, splits used).  With fused_q an e4m3 workload hands bf16 Q to the attention call, which
-    quantizes it itself (no codes are returned then)."""
+    quantizes it itself (no codes are returned then).  With split_q a bf16 workload runs QK^T on
+    the FP8 MFMA with Q split into two E4M3 terms (q_dtype BF16_SPLIT)."""
     import fp8_kv_cache_e4m3_amd as fa
     dev = torch.device("cuda")
     wd = w.to(dev)
@@ -84,8 +85,9 @@ def gpu_run(w: wl.Workload, entry="decode", num_splits=0, window=None, softmax_s
     else:
         q, qd = wd.q, None
     win = w.window if window is None else window
+    assert not split_q or w.q_dtype == "bf16", "split Q takes bf16 queries"
     kw = dict(q_descale=qd, k_descale=wd.k_descale, v_descale=wd.v_descale, softmax_scale=softmax_scale,
-              window=win, want_lse=want_lse, out=out, quantize_q=fused_q)
+              window=win, want_lse=want_lse, out=out, quantize_q=fused_q, split_q=split_q)
     args = (q, wd.k_pool, wd.v_pool, wd.block_table, wd.cu_seqlens_q, wd.seqlens_k, w.max_seqlen_q,
             w.max_seqlen_k)
     splits = 1

@@ -73,7 +73,7 @@ def _status(a, fn="prefill"):
 @pytest.mark.parametrize("fn", ["prefill", "decode"])
 @pytest.mark.parametrize("change,status,words", [
     ({"causal": 0}, fa.ERR_UNSUPPORTED, ["non-causal", "q=bf16", "head_size=512"]),
-    ({"head_dim": 256}, fa.ERR_UNSUPPORTED, ["q=bf16", "k=e4m3", "v=e4m3", "head_size=256", "head_size_v=256"]),
+    ({"head_dim": 320}, fa.ERR_UNSUPPORTED, ["q=bf16", "k=e4m3", "v=e4m3", "head_size=320", "head_size_v=320"]),
     ({"q_dtype": fa.E4M3, "head_dim": 512}, fa.ERR_UNSUPPORTED, ["q=e4m3", "head_size=512"]),
     ({"q_dtype": fa.BF16_TO_E4M3, "head_dim": 512}, fa.ERR_UNSUPPORTED, ["q=bf16->e4m3", "head_size=512"]),
     ({"head_dim": 80}, fa.ERR_UNSUPPORTED, ["head_size=80"]),
@@ -108,12 +108,23 @@ def test_rejections(fn, change, status, words):
 @pytest.mark.parametrize("q_dtype", [fa.E4M3, fa.BF16_TO_E4M3])
 @pytest.mark.parametrize("head_dim", [64, 96, 128, 192, 256])
 def test_quantized_q_modes_pass_validation(fn, q_dtype, head_dim):
-    # Both quantized-query modes are accepted at head_size 64 and 256, with or without a
+    # Both quantized-query modes are accepted at every native-FP8 head size, with or without a
     # q_descale; an empty batch then returns OK without touching the device.
     for qd in (0, 0x1000):
         a, keep = _valid_args(q_dtype=q_dtype, head_dim=head_dim, q_descale=qd, batch=0, total_q=0)
         st = _status(a, fn)
         assert st == fa.OK, (st, fa.fp8attn_last_error())
+
+
+@pytest.mark.parametrize("fn", ["prefill", "decode"])
+@pytest.mark.parametrize("head_dim", [64, 96, 128, 192, 256, 512])
+def test_split_q_mode_validation(fn, head_dim):
+    # split Q takes every head dim and unquantized queries: a q_descale is rejected
+    a, keep = _valid_args(q_dtype=fa.BF16_SPLIT, head_dim=head_dim, batch=0, total_q=0)
+    assert _status(a, fn) == fa.OK, fa.fp8attn_last_error()
+    a, keep = _valid_args(q_dtype=fa.BF16_SPLIT, head_dim=head_dim, q_descale=0x1000)
+    assert _status(a, fn) == fa.ERR_UNSUPPORTED
+    assert "q=bf16-split" in fa.fp8attn_last_error() and "q_descale must be NULL" in fa.fp8attn_last_error()
 
 
 def test_decode_rejects_long_query():

@@ -308,6 +308,46 @@ def test_head_dims(d, q_dtype, entry, splits):
         assert s1 == s and np.array_equal(o1, o) and np.array_equal(l1, l)
 
 
+# ------------------------------------------------------------------------------------------
+# split Q (q_dtype BF16_SPLIT): bf16 queries on the FP8 MFMA as hi + lo/16, every head dim and
+# plan; against the oracle (bf16 Q values exactly) and against the BF16-MFMA path, which takes
+# the same exact Q values (outputs differ only by the order of fp32 sums)
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("d", [64, 96, 128, 192, 256, 512])
+@pytest.mark.parametrize("entry,splits", [("decode", 0), ("decode", 3), ("decode", -5), ("prefill", 0)])
+def test_split_q(d, entry, splits):
+    window = -1 if d in (96, 512) else 200
+    if entry == "decode":
+        w = wl.custom("bf16", d, 16, 2, window, [700, 65, 1500], [4, 16, 1], seed=d + 5)
+    else:
+        w = wl.custom("bf16", d, 8, 2, window, [600, 90, 700], [300, 90, 41], seed=d + 6)
+    log(f"[case] split-q d{d} {entry} splits={splits}")
+    o_ref, l_ref, _ = oracle_run(w)
+    o, l, _, s = gpu_run(w, entry, num_splits=splits, split_q=True)
+    compare(o, o_ref, l, l_ref, label=f"split-q d{d} {entry} S={s}")
+    o_b, l_b, _, s_b = gpu_run(w, entry, num_splits=splits)
+    assert s_b == s
+    assert np.max(np.abs(o - o_b)) <= 8e-3 and np.max(np.abs(l - l_b)) <= 1e-4, \
+        (np.max(np.abs(o - o_b)), np.max(np.abs(l - l_b)))
+
+
+def test_split_q_row_scales():
+    """Per-row power-of-two scales: query rows of magnitude 0, 1e-30, 1e-3, 1, 1e3 and 1e30 (the
+    large ones give one-hot softmax rows, the tiny ones near-uniform rows)."""
+    w = wl.custom("bf16", 512, 8, 2, -1, [900, 300, 77], [2, 2, 2], seed=33)
+    mags = [0.0, 1e-30, 1e-3, 1.0, 1e3, 1e30]
+    q = w.q.float()
+    for t in range(q.shape[0]):
+        q[t] *= mags[t % len(mags)]
+    w.q = q.to(torch.bfloat16)
+    o_ref, l_ref, _ = oracle_run(w)
+    o, l, _, _ = gpu_run(w, "decode", split_q=True)
+    compare(o, o_ref, label="split-q row scales")
+    # The LSE of the 1e30 rows is their largest logit, about 1e32: an fp32 sum of 512 products
+    # with cancellation, so its error is relative (measured 1.4e-5), bounded here by 1e-4
+    assert np.all(np.abs(l - l_ref) <= 1e-2 + 1e-4 * np.abs(l_ref)), np.max(np.abs(l - l_ref) / (1 + np.abs(l_ref)))
+
+
 def test_page_size_128_and_strided_output():
     """Framework blocks of 128 tokens (two kernel pages) and an output with padded strides."""
     fa = _fa()

@@ -134,3 +134,29 @@ def test_dequantize_and_descale_recipe():
     codes = quantize_e4m3(x, ds)
     assert codes[1] == 0xFE                                # amax maps to -448
     assert dequantize_e4m3(codes[1:2], ds)[0] == -448.0 * float(ds)
+
+
+def test_two_e4m3_terms_hold_every_bf16_value():
+    """Why split Q (hi + lo/16 on the FP8 MFMA) gives the BF16 product: for every finite bf16
+    value x and the power-of-two row scale 2^e that brings the row's largest magnitude into
+    (224, 448], hi = E4M3(x 2^e) and lo = E4M3(16 (x 2^e - hi)) satisfy hi + lo/16 == x 2^e
+    exactly whenever |x 2^e| >= 2^-6 (E4M3's smallest normal): x has 8 significant bits, hi
+    keeps the top 4, the residual has at most 4.  Below that the error stays under 2^-13."""
+    import torch
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    with np.errstate(invalid="ignore"):
+        x = bits.float().numpy().astype(np.float64)
+    x = x[np.isfinite(x) & (x != 0)]
+    for amax_exp in (-100, -3, 0, 7, 60, 127):            # rows of very different magnitudes
+        amax = 2.0 ** amax_exp * 1.7
+        e = int(np.floor(np.log2(448.0 / amax)))
+        row = x[np.abs(x) <= amax]
+        xs = (row * 2.0 ** e).astype(np.float32)           # exact: a power-of-two scale
+        hi = quantize_e4m3(xs)
+        r = (xs.astype(np.float64) - dequantize_e4m3(hi)) * 16.0
+        assert np.all(r.astype(np.float32) == r)           # the residual is an exact fp32 value
+        lo = quantize_e4m3(r.astype(np.float32))
+        back = dequantize_e4m3(hi) + dequantize_e4m3(lo) / 16.0
+        normal = np.abs(xs) >= 2.0 ** -6
+        assert np.all(back[normal] == xs[normal]), amax_exp
+        assert np.max(np.abs(back - xs)) <= 2.0 ** -13

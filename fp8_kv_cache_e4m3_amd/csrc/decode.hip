@@ -383,7 +383,10 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
   };
 
   // mask, online softmax update, P^T operand of unit u (lane (row, g) holds keys 4g..4g+3)
-  auto softmax = [&](const f32x4_t sacc, int u) __attribute__((always_inline)) -> bf16x4_t {
+  // split Q also runs PV on the FP8 MFMA, with P <= 2^4 (see compute); the other modes keep
+  // P <= 2^8
+  constexpr float kLazy = SPLIT ? 4.0f : kLazyMax;
+  auto softmax = [&](const f32x4_t sacc, int u) __attribute__((always_inline)) -> f32x4_t {
     float sv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sv[i] = sacc[i] * cs;
@@ -401,7 +404,7 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
     // Lazy running max: it moves only when a unit exceeds it by more than 2^8, so P <= 256 and
     // the O rescale (64 accumulators) is rare after the first unit.  A row whose max is still
     // -inf has O = 0 and l = 0, so its first move needs no rescale of O.
-    const bool grow = mx > m_run + kLazyMax;
+    const bool grow = mx > m_run + kLazy;
     if (__any(grow)) {
       const float m_new = grow ? mx : m_run;
       const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));   // 1 where not grown
@@ -417,14 +420,35 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
 #pragma unroll
     for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(sv[i] - m_use);
     l_run += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-    return bf16x4_t{(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
+    return f32x4_t{pv[0], pv[1], pv[2], pv[3]};
   };
 
   // O^T += V^T * P^T with V in registers (lane (col, g) holds bytes col*CW.. of keys 4g..4g+3):
   // a 4x4 byte transpose gives, per O^T tile t, row col <-> d = 16 col + t (d256) or the
   // analogous interleave (d64, d512)
+  //
+  // Split Q runs PV on the FP8 MFMA too, at the precision of bf16 P: each P (<= 2^4) is written
+  // as 16 hi + lo with hi = E4M3(P) and lo = E4M3(16 (P - hi)); 16 hi is exact and at most 256.
+  // One 16x16x32 MFMA per O^T tile takes the lane's 4 keys twice, 16 hi in byte slots 0-3 and
+  // lo in slots 4-7, against the same 4 V bytes in both halves of the A operand, so it
+  // accumulates 16 O; the 1/16 goes into the final 1/l.
   auto compute = [&](const UnitRegs<DP>& ur, int u) __attribute__((always_inline)) {
-    const bf16x4_t pb = softmax(qk(ur.k), u);
+    const f32x4_t pf = softmax(qk(ur.k), u);
+    uint64_t p8 = 0;
+    bf16x4_t pb = {};
+    if constexpr (SPLIT) {
+      int hc = __builtin_amdgcn_cvt_pk_fp8_f32(pf[0], pf[1], 0, false);
+      hc = __builtin_amdgcn_cvt_pk_fp8_f32(pf[2], pf[3], hc, true);
+      const f32x2_t h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hc, false);
+      const f32x2_t h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hc, true);
+      int h16 = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * h01[0], 16.0f * h01[1], 0, false);
+      h16 = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * h23[0], 16.0f * h23[1], h16, true);
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * (pf[0] - h01[0]), 16.0f * (pf[1] - h01[1]), 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * (pf[2] - h23[0]), 16.0f * (pf[3] - h23[1]), lo, true);
+      p8 = (uint64_t)(uint32_t)h16 | ((uint64_t)(uint32_t)lo << 32);
+    } else {
+      pb = bf16x4_t{(__bf16)pf[0], (__bf16)pf[1], (__bf16)pf[2], (__bf16)pf[3]};
+    }
 #pragma unroll
     for (int blk = 0; blk < S::VBLK; ++blk) {
 #pragma unroll
@@ -435,7 +459,10 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = blk * S::CW + 4 * w + e;
-          oacc[t] = mfma_bf16_16x16x16(e4m3x4_to_bf16(tr[e]), pb, oacc[t]);
+          if constexpr (SPLIT)
+            oacc[t] = mfma_fp8_16x16x32((uint64_t)tr[e] | ((uint64_t)tr[e] << 32), p8, oacc[t]);
+          else
+            oacc[t] = mfma_bf16_16x16x16(e4m3x4_to_bf16(tr[e]), pb, oacc[t]);
         }
       }
     }
@@ -512,7 +539,7 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
       }
       const int tk = t0 + rr / G;
       const int hh = h * G + rr % G;
-      const float inv = Ls > 0.f ? vd / Ls : 0.f;
+      const float inv = Ls > 0.f ? vd / (SPLIT ? 16.0f * Ls : Ls) : 0.f;   // (split Q accumulates 16 O)
       const float lse2 = Ls > 0.f ? (M + fast_log2(Ls)) : kNegInf;
       if (whole) {
         __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)tk * p.out_stride_tok +

@@ -65,7 +65,9 @@ typedef enum fp8attn_dtype {
                                     every value above about 2^-14 of the row's largest; QK^T is
                                     the two-part sum K.hi + K.lo/16, times 2^-e ([60372] review
                                     thread: the d512 FP8-MMA kernel keeps BF16 queries and builds
-                                    a split QK accumulation).  No q_descale.  (q only) */
+                                    a split QK accumulation).  PV runs on the FP8 MFMA too, with
+                                    P as two E4M3 terms (8 significant bits, as bf16 P).  No
+                                    q_descale.  (q only) */
 } fp8attn_dtype;
 
 /*

@@ -309,9 +309,11 @@ def test_head_dims(d, q_dtype, entry, splits):
 
 
 # ------------------------------------------------------------------------------------------
-# split Q (q_dtype BF16_SPLIT): bf16 queries on the FP8 MFMA as hi + lo/16, every head dim and
-# plan; against the oracle (bf16 Q values exactly) and against the BF16-MFMA path, which takes
-# the same exact Q values (outputs differ only by the order of fp32 sums)
+# split Q (q_dtype BF16_SPLIT): QK^T on the FP8 MFMA with Q as hi + lo/16 (exact for bf16) and
+# PV on the FP8 MFMA with P as 16 hi + lo (8 significant bits, like bf16 P), every head dim and
+# plan; against the oracle and against the BF16-MFMA path: the same exact Q values and P kept
+# to 8 bits in both, rounded differently, so outputs agree to two bf16 ulps and the LSE (which
+# takes fp32 P in both) to the order of fp32 sums
 # ------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("d", [64, 96, 128, 192, 256, 512])
 @pytest.mark.parametrize("entry,splits", [("decode", 0), ("decode", 3), ("decode", -5), ("prefill", 0)])
@@ -327,7 +329,7 @@ def test_split_q(d, entry, splits):
     compare(o, o_ref, l, l_ref, label=f"split-q d{d} {entry} S={s}")
     o_b, l_b, _, s_b = gpu_run(w, entry, num_splits=splits)
     assert s_b == s
-    assert np.max(np.abs(o - o_b)) <= 8e-3 and np.max(np.abs(l - l_b)) <= 1e-4, \
+    assert np.max(np.abs(o - o_b)) <= 1.6e-2 and np.max(np.abs(l - l_b)) <= 1e-4, \
         (np.max(np.abs(o - o_b)), np.max(np.abs(l - l_b)))
 
 

@@ -13,15 +13,17 @@
 //                   QK^T on the FP8 MFMA as a two-part accumulation (vLLM PR #60372, review
 //                   thread: the d512 FP8-MMA kernel keeps BF16 queries and builds a split QK
 //                   accumulation; the split itself is not described there, see split8_bf16_e4m3).
-// PV runs on the BF16 MFMA in both variants: V bytes are dequantized exactly to bf16 and P is
-// rounded once to bf16.  Decode is HBM-bound, so the cheaper FP8 PV would not move the time but
-// would cost accuracy on short rows.
+// PV runs on the BF16 MFMA in the first three modes: V bytes are dequantized exactly to bf16 and
+// P is rounded once to bf16.  Decode is HBM-bound, so the cheaper FP8 PV would not move the time,
+// and plain E4M3 P would cost accuracy on short rows.  Split Q runs PV on the FP8 MFMA with P as
+// two E4M3 terms, as many significant bits as bf16 P (see compute).
 //
 // Design (gfx950, wave64):
-//  * Work item = (kv head, split, sequence, row tile), XCD-aware block order.  4 waves per
-//    block; each wave streams its own 16-key units (a quarter of the split) straight from HBM
-//    into registers, with the next unit's loads in flight while the current one is computed.
-//    No LDS staging and no barriers in the main loop.
+//  * Work item = (kv head, split, sequence, row tile), XCD-aware block order, or a range of the
+//    balanced partition (decode_balanced_kernel).  4 waves per block; each wave streams its own
+//    16-key units (a quarter of the range) straight from HBM into registers, with the next
+//    unit's loads in flight while the current one is computed.  No LDS staging and no barriers
+//    in the main loop.
 //  * S^T = K * Q^T: the 16 keys are MFMA rows, the 16 query rows are MFMA columns, so every
 //    query row lives on one lane column (lane % 16) and its softmax state is per lane.
 //  * O^T = V^T * P^T: P^T comes straight out of the S^T accumulator layout (lane (r, g) holds

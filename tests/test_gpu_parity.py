@@ -88,16 +88,19 @@ def test_workload_reduced_all_rows(name, scale, entry):
     compare(o, o_ref, l, l_ref, label=f"{w.name} S={splits}")
 
 
-@pytest.mark.parametrize("name,entry,nsample", [
-    ("swa_decode", "decode", 32),
-    ("full_decode", "decode", 8),
-    ("spec_verify", "decode", 8),
-    ("swa_prefill", "prefill", 24),
+@pytest.mark.parametrize("name,entry,nsample,split_q", [
+    ("swa_decode", "decode", 32, False),
+    ("full_decode", "decode", 8, False),
+    ("spec_verify", "decode", 8, False),
+    ("swa_prefill", "prefill", 24, False),
+    ("full_decode", "decode", 8, True),      # bf16 Q on the FP8 MFMA (split Q)
+    ("spec_verify", "decode", 8, True),
 ])
-def test_workload_full_size_sampled(name, entry, nsample):
+def test_workload_full_size_sampled(name, entry, nsample, split_q):
     w = wl.BY_NAME[name](device="cuda")
-    log(f"[case] full-size {w.name} entry={entry} B={w.batch} total_q={w.total_q} pool={tuple(w.k_pool.shape)}")
-    o, l, codes, splits = gpu_run(w, entry)
+    log(f"[case] full-size {w.name} entry={entry} split_q={split_q} B={w.batch} total_q={w.total_q} "
+        f"pool={tuple(w.k_pool.shape)}")
+    o, l, codes, splits = gpu_run(w, entry, split_q=split_q)
     if codes is not None:   # bit-exact quantization over the whole Q tensor
         _, codes_ref = __import__("oracle").attention.query_values(w.q.cpu(), "e4m3", w.q_descale.cpu())
         assert np.array_equal(codes, codes_ref)

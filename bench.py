@@ -408,6 +408,10 @@ def main():
             # the same bf16-Q workloads with QK^T on the FP8 MFMA (split Q)
             ("full_decode_split_q", lambda s: wl.full_decode(device="cuda", seed=200 + s), "decode", 4, "hbm", True),
             ("spec_verify_split_q", lambda s: wl.spec_verify(device="cuda", seed=300 + s), "decode", 2, "hbm", True),
+            # d512 prefill (BF16 Q and split Q): the decode kernel over 16-row tiles, no MFMA prefill kernel
+            ("full_prefill", lambda s: wl.full_prefill(device="cuda", seed=500 + s), "prefill", 2, "mfma", False),
+            ("full_prefill_split_q", lambda s: wl.full_prefill(device="cuda", seed=500 + s), "prefill", 2, "mfma",
+             True),
         ]
         for name, make, entry, ns, bound, split in specs:
             r = time_workload(make, entry, ns, max(5, args.steps // 5), 2, name, fused, split)
@@ -426,7 +430,7 @@ def main():
             if bound == "hbm":
                 e["hbm_frac"] = round(e["kv_read_GBps"] / HBM_PEAK_GBS, 4)
             else:
-                peak = FP8_PEAK_TFLOPS if ww.q_dtype == "e4m3" else BF16_PEAK_TFLOPS
+                peak = FP8_PEAK_TFLOPS if ww.q_dtype == "e4m3" or split else BF16_PEAK_TFLOPS
                 e["mfma_frac"] = round(e["TFLOPs"] / peak, 4)
             extra[name] = e
         for name, make, ns in [("swa_decode_graph", lambda s: wl.swa_decode(device="cuda", seed=100 + s), nsets),

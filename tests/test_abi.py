@@ -225,3 +225,24 @@ def test_cache_write_rejections():
     assert call(args(T=0)) == fa.OK
     assert call(args(k=0x1008, v=0x2000, slots=0x3000, kc=0x4000, vc=0x5000)) == fa.ERR_UNSUPPORTED
     assert "aligned" in fa.fp8attn_last_error()
+
+
+def test_last_error_is_per_thread():
+    # each thread reads the message of its own last failed call, whatever the other thread did
+    import threading
+    results = {}
+
+    def worker(name, change, word):
+        a, keep = _valid_args(**change)
+        for _ in range(200):
+            st = _status(a, "prefill")
+            msg = fa.fp8attn_last_error()
+            if st == fa.OK or word not in msg:
+                results[name] = (st, msg)
+                return
+        results[name] = "ok"
+
+    t1 = threading.Thread(target=worker, args=("a", {"causal": 0}, "non-causal"))
+    t2 = threading.Thread(target=worker, args=("b", {"window": 0}, "window must be"))
+    t1.start(); t2.start(); t1.join(); t2.join()
+    assert results == {"a": "ok", "b": "ok"}, results

@@ -70,19 +70,21 @@ def test_tiny_case(q_dtype, entry):
 
 
 # ------------------------------------------------------------------------------------------
-# the four performance workloads: reduced sizes element by element, full sizes on samples
+# the performance workloads: reduced sizes element by element, full sizes on samples
 # ------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("name,scale,entry", [
-    ("swa_decode", 0.25, "decode"),
-    ("full_decode", 0.125, "decode"),
-    ("spec_verify", 0.0625, "decode"),
-    ("swa_prefill", 1 / 32, "prefill"),
+@pytest.mark.parametrize("name,scale,entry,split_q", [
+    ("swa_decode", 0.25, "decode", False),
+    ("full_decode", 0.125, "decode", False),
+    ("spec_verify", 0.0625, "decode", False),
+    ("swa_prefill", 1 / 32, "prefill", False),
+    ("full_prefill", 1 / 8, "prefill", False),
+    ("full_prefill", 1 / 8, "prefill", True),
 ])
-def test_workload_reduced_all_rows(name, scale, entry):
+def test_workload_reduced_all_rows(name, scale, entry, split_q):
     w = wl.BY_NAME[name](device="cpu", scale=scale)
-    log(f"[case] {w.name} entry={entry} B={w.batch} total_q={w.total_q} maxL={w.max_seqlen_k}")
+    log(f"[case] {w.name} entry={entry} split_q={split_q} B={w.batch} total_q={w.total_q} maxL={w.max_seqlen_k}")
     o_ref, l_ref, codes_ref = oracle_run(w)
-    o, l, codes, splits = gpu_run(w, entry)
+    o, l, codes, splits = gpu_run(w, entry, split_q=split_q)
     if codes is not None:
         assert np.array_equal(codes, codes_ref)
     compare(o, o_ref, l, l_ref, label=f"{w.name} S={splits}")
@@ -95,6 +97,8 @@ def test_workload_reduced_all_rows(name, scale, entry):
     ("swa_prefill", "prefill", 24, False),
     ("full_decode", "decode", 8, True),      # bf16 Q on the FP8 MFMA (split Q)
     ("spec_verify", "decode", 8, True),
+    ("full_prefill", "prefill", 16, False),
+    ("full_prefill", "prefill", 16, True),
 ])
 def test_workload_full_size_sampled(name, entry, nsample, split_q):
     w = wl.BY_NAME[name](device="cuda")
@@ -375,11 +379,12 @@ def test_page_size_128_and_strided_output():
     o_ref, l_ref, _ = oracle_run(w)
     w2 = wl.Workload(**{**w.__dict__})
     w2.k_pool, w2.v_pool, w2.block_table = k2, v2, table
-    big = torch.zeros((w.total_q, 8, 640), dtype=torch.bfloat16, device="cuda")
-    out = big[:, :, 64:576]
-    o, l, _, _ = gpu_run(w2, "decode", num_splits=2, out=out)
-    compare(o, o_ref, l, l_ref, label="page 128 + strided out")
-    assert torch.all(big[:, :, :64] == 0) and torch.all(big[:, :, 576:] == 0), "wrote outside the output view"
+    for splits in (2, -5):   # split grid and balanced partition
+        big = torch.zeros((w.total_q, 8, 640), dtype=torch.bfloat16, device="cuda")
+        out = big[:, :, 64:576]
+        o, l, _, _ = gpu_run(w2, "decode", num_splits=splits, out=out)
+        compare(o, o_ref, l, l_ref, label=f"page 128 + strided out, splits {splits}")
+        assert torch.all(big[:, :, :64] == 0) and torch.all(big[:, :, 576:] == 0), "wrote outside the output view"
 
 
 def test_per_sequence_head_descales():

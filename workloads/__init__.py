@@ -244,6 +244,16 @@ def swa_prefill(device="cpu", layout: str = "token_major", seed: int = 4, scale:
                      [L] * B, [L] * B, layout=layout)
 
 
+def full_prefill(device="cpu", layout: str = "token_major", seed: int = 6, scale: float = 1.0) -> Workload:
+    """Prefill of full-attention layers: 4 sequences of 2048 new tokens each (no prior cache),
+    32 q / 4 kv heads (GQA 8), d 512, bf16 Q with E4M3 K/V, causal."""
+    rng = _Rng(seed, device)
+    B = max(1, int(round(4 * scale)))
+    L = max(1, int(2048 * scale))
+    return _assemble(f"full-attention prefill B{B}x{L} d512", rng, "bf16", 512, 32, 4, -1,
+                     [L] * B, [L] * B, layout=layout)
+
+
 def spec_verify(device="cpu", layout: str = "token_major", seed: int = 5, scale: float = 1.0) -> Workload:
     """Spec-decode verify with a shared prefix: 64 sequences, each a 25,600-token prefix whose
     pages every sequence shares, plus 3,072 unique tokens; 4 query tokens (1 + 3 speculative)
@@ -271,4 +281,5 @@ BY_NAME = {
     "full_decode": full_decode,
     "swa_prefill": swa_prefill,
     "spec_verify": spec_verify,
+    "full_prefill": full_prefill,
 }

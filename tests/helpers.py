@@ -7,7 +7,6 @@ arrays bit for bit.
 """
 from __future__ import annotations
 
-import math
 import sys
 
 import numpy as np

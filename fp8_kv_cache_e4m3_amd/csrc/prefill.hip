@@ -133,14 +133,15 @@ __device__ __forceinline__ void tile_load_step(const TileLoad& tl, const uint32_
 //    is the source row this lane supplies; vp already holds the lane's part of the address.
 //  * QK op (h2, c): key rows 32*h2 + kperm(m) (kp holds the lane's row and half), d bytes
 //    64c .. 64c + 63.  The two 32-key halves alternate so consecutive MFMAs are independent.
-template <int D, bool SPLIT>
+// DO_PV / DO_QK leave out the PV or the QK^T half: a wave skips a tile none of its rows sees.
+template <int D, bool SPLIT, bool DO_PV, bool DO_QK>
 __device__ __forceinline__ void mfma_stream(const uint8_t* vp, const uint8_t* kp,
                                             f32x16_t (&oacc)[PrefillShape<D>::NDT], f32x16_t (&sacc)[2],
                                             const i32x8_t& pb, const i32x8_t& pbl,
                                             const i32x8_t (&qop)[PrefillShape<D>::KSTEP]) {
   using S = PrefillShape<D>;
-  constexpr int NPV = S::NDT;
-  constexpr int NOPS = NPV + 2 * S::KSTEP;
+  constexpr int NPV = DO_PV ? S::NDT : 0;
+  constexpr int NOPS = NPV + (DO_QK ? 2 * S::KSTEP : 0);
   i32x8_t buf[3];
 #pragma unroll
   for (int j = 0; j < NOPS + 2; ++j) {
@@ -227,6 +228,9 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   const int wpf = L - ql + (wave_active ? wr0 : rlast) / G;
   const int wpl = L - ql + (wave_active ? wrl : rlast) / G;
   const int wfull_lo = W >= 1 ? wpl - W + 1 : 0;     // keys [wfull_lo, wpf] are visible to every row
+  // tiles holding a key that some row of the wave sees (wave-uniform)
+  const int wt0 = __builtin_amdgcn_readfirstlane((W >= 1 ? max(0, wpf - W + 1) : 0) / S::BK);
+  const int wt1 = __builtin_amdgcn_readfirstlane(wave_active ? wpl / S::BK : kt0 - 1);
   // this lane's row
   const int r = wr0 + lr;
   const bool rvalid = r < nrows;
@@ -317,7 +321,6 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   const int tr_j = (lane & 15) >> 1;         // source row j (0..7) supplied by this lane
   const int tr_h = lane & 1;                 // 8-byte half of the 16-byte chunk
 
-  // S^T = K * Q^T for tile kt (K tile in stage st)
   // S^T = K * Q^T for tile kt (K tile in stage st).  A operand row m holds key kperm(m).
   const int k_lane = lane_offset(kperm(lr) * S::RS + 32 * lg);
 
@@ -395,11 +398,16 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   // 32 keys per lane.  Slots 8q..8q+7 of lane group lg hold the 8 consecutive keys
   // 32(q/2) + 16(q%2) + 8*lg + j, where j is the source row this lane supplies to the read.
   const int v_lane = lane_offset((8 * lg + tr_j) * S::RS + (D / 2) * tr_blk + 8 * tr_h);
-  // MFMA work between two barriers: PV of the tile in stage so_v, then QK^T of the tile in stage
-  // so_k.  Every step runs both halves: where a step has no PV (before the first tile) P is
-  // still zero, and where it has no QK^T (after the last tile) S is not used again.
-  auto run_stream = [&](int so_v, int so_k) __attribute__((always_inline)) {
-    mfma_stream<D, SPLIT>(lds + (so_v + S::TILE + v_lane), lds + (so_k + k_lane), oacc, sacc, pb, pbl, qop);
+  // MFMA work between two barriers: PV of tile tv (stage so_v), then QK^T of tile tk (stage so_k).
+  // A half runs only for a tile inside the wave's tile range [wt0, wt1]: a tile outside it is
+  // masked for every row of the wave (P = 0), so its PV adds nothing and its S is never used.
+  // (Before the first tile and after the last one the tile index is outside the range too.)
+  auto run_stream = [&](int so_v, int so_k, int tv, int tk) __attribute__((always_inline)) {
+    const uint8_t* vp = lds + (so_v + S::TILE + v_lane);
+    const uint8_t* kp = lds + (so_k + k_lane);
+    const bool pv = tv >= wt0 && tv <= wt1, qk = tk >= wt0 && tk <= wt1;
+    if (pv) mfma_stream<D, SPLIT, true, false>(vp, kp, oacc, sacc, pb, pbl, qop);
+    if (qk) mfma_stream<D, SPLIT, false, true>(vp, kp, oacc, sacc, pb, pbl, qop);
     // S is needed in this half period: keep the compiler from sinking the QK^T MFMAs past the
     // barrier that may follow
     asm volatile("" ::"v"(sacc[0]), "v"(sacc[1]));
@@ -415,7 +423,6 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   // tile's loads have more than an interval to land.  Before each barrier a wave waits for all
   // its loads but the ones of the interval that ends there.  Loads past the last tile read one
   // cache line into the free stage, which keeps the number of loads the same every interval.
-  const bool grpB = wave >= S::NW / 2;
   // Before a barrier: the loads older than this interval's have landed.  Also a scheduling fence:
   // the compiler may not move the softmax or MFMA work of one half period across the barrier into
   // the other half, which would take away the overlap.
@@ -465,24 +472,25 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   interval_loads(kt0 - 1);
   // Every wave processes every tile of the block; tiles outside a wave's key range are fully
   // masked for its rows (P = 0), which keeps the loop body one straight MFMA stream.
+  const bool grpB = wave >= S::NW / 2;
   if (!grpB) {
-    run_stream(stage_of(kt0), stage_of(kt0));   // QK^T of the first tile (P is zero: PV adds nothing)
+    run_stream(stage_of(kt0), stage_of(kt0), kt0 - 1, kt0);   // QK^T of the first tile
     for (int t = kt0; t <= kt1; ++t) {
-      softmax(t);
+      if (t >= wt0 && t <= wt1) softmax(t);
       wait_loads();
       __syncthreads();
       interval_loads(t);                         // interval t
-      run_stream(stage_of(t), stage_of(t + 1));
+      run_stream(stage_of(t), stage_of(t + 1), t, t + 1);
     }
   } else {
     // the stream at step t belongs to interval t - 1; one step past the last tile finishes PV
     // of the last tile
     for (int t = kt0; t <= kt1 + 1; ++t) {
-      run_stream(t > kt0 ? stage_of(t - 1) : stage_of(t), stage_of(t));
+      run_stream(t > kt0 ? stage_of(t - 1) : stage_of(t), stage_of(t), t - 1, t);
       if (t <= kt1) {
         wait_loads();
         __syncthreads();
-        softmax(t);
+        if (t >= wt0 && t <= wt1) softmax(t);
         interval_loads(t);                       // interval t
       }
     }

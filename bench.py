@@ -273,6 +273,47 @@ def time_cache_write(make, steps, label):
             "traffic": load_traffic(label) if label == "kv_write_swa_prefill" else None}
 
 
+def time_quantize(shape, steps, label):
+    """fp8attn_quantize_q on a bf16 Q of the given shape [tokens, heads, d] (values N(0,1),
+    per-tensor descale amax/448), timed with events around `steps` back-to-back calls that
+    alternate between two input sets.  Algorithmic bytes: bf16 in, E4M3 codes out."""
+    import torch
+    import fp8_kv_cache_e4m3_amd as fa
+    sets = []
+    for seed in range(2):
+        g = torch.Generator(device="cuda").manual_seed(600 + seed)
+        q = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+        ds = (q.float().abs().amax() / 448.0).reshape(1)
+        out = torch.empty(shape, dtype=torch.uint8, device="cuda")
+        sets.append((q, ds, out))
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def call(i):
+        q, ds, out = sets[i % 2]
+        st = fa.LIB.fp8attn_quantize_q(q.data_ptr(), q.shape[0], q.shape[1], q.shape[2], q.stride(0), q.stride(1),
+                                       ds.data_ptr(), out.data_ptr(), sh)
+        assert st == 0, fa.fp8attn_last_error()
+    for i in range(4):
+        call(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(steps):
+        call(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    n = sets[0][0].numel()
+    nbytes = 3 * n
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] {label}: {tuple(shape)}: {ms:.4f} ms, {gbs:.0f} GB/s")
+    del sets
+    torch.cuda.empty_cache()
+    return {"workload": f"quantize_q, bf16 Q {list(shape)}", "ms_per_call": round(ms, 4), "GBps": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}
+
+
 def cpu_baseline(budget_s=15.0):
     """The CPU oracle, as is, on a bounded sample of the sliding-window decode workload: whole
     sequences (all 32 q heads) until the time budget is spent.  Rate = the same algorithmic bytes
@@ -439,6 +480,9 @@ def main():
         for name, make in [("kv_write_swa_prefill", lambda s: wl.swa_prefill(device="cuda", seed=400 + s)),
                            ("kv_write_swa_decode", lambda s: wl.swa_decode(device="cuda", seed=100 + s))]:
             extra[name] = time_cache_write(make, max(5, args.steps // 5), name)
+        # the stand-alone Q quantization (the steps above quantize inside the attention kernels)
+        extra["quantize_q_swa_prefill"] = time_quantize((65536, 32, 256), max(5, args.steps // 5),
+                                                        "quantize_q_swa_prefill")
 
     cpu = None
     if not args.no_cpu:

@@ -20,6 +20,16 @@ namespace fp8attn {
 
 // CONTIG: Q rows (token, head) are back to back (head stride d, token stride heads * d), so the
 // input vector index is the output one and no index arithmetic is needed.
+//
+// Each thread issues kQuantUnroll 16-byte loads (vectors v and v + T for T threads in the grid,
+// so every load instruction of a wave is one contiguous 1 KiB) before the first conversion, and
+// the grid has a block per 256 * kQuantUnroll vectors: one trip through the loop per thread.  A
+// grid capped at 64 blocks per CU, each thread looping over several trips with one load at a
+// time, reached 4.8 TB/s on the 1 GiB prefill Q; this shape reaches 6.0-6.2 TB/s, the rate of
+// torch's own bf16 -> E4M3 cast over the same bytes.  Loads and stores are non-temporal: every
+// byte is touched once.
+constexpr int kQuantUnroll = 2;
+
 template <bool CONTIG>
 __global__ void __launch_bounds__(256) quantize_q_kernel(const __bf16* __restrict__ q, int64_t nvec,
                                                          int32_t nheads, int32_t vec_per_head,
@@ -28,18 +38,29 @@ __global__ void __launch_bounds__(256) quantize_q_kernel(const __bf16* __restric
                                                          uint8_t* __restrict__ out) {
   const float ds = q_descale ? q_descale[0] : 1.0f;
   const double rcp = 1.0 / (double)ds;   // correctly rounded fp64 reciprocal
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
-    int64_t src = v * 8;
-    if constexpr (!CONTIG) {
-      const int64_t c = v % vec_per_head;
-      const int64_t th = v / vec_per_head;
-      const int64_t hd = th % nheads;
-      const int64_t tok = th / nheads;
-      src = tok * stride_tok + hd * stride_head + c * 8;
+  const int64_t nthr = (int64_t)gridDim.x * blockDim.x;
+  auto src_of = [&](int64_t v) __attribute__((always_inline)) -> int64_t {
+    if constexpr (CONTIG) return v * 8;
+    const int64_t c = v % vec_per_head;
+    const int64_t th = v / vec_per_head;
+    const int64_t hd = th % nheads;
+    const int64_t tok = th / nheads;
+    return tok * stride_tok + hd * stride_head + c * 8;
+  };
+  for (int64_t v0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v0 < nvec; v0 += kQuantUnroll * nthr) {
+    u32x4_t w[kQuantUnroll];
+#pragma unroll
+    for (int k = 0; k < kQuantUnroll; ++k) {
+      const int64_t v = v0 + k * nthr;
+      w[k] = v < nvec ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(q + src_of(v)))
+                      : u32x4_t{0, 0, 0, 0};
     }
-    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(q + src);
-    *reinterpret_cast<u32x2_t*>(out + v * 8) = quantize8_bf16_e4m3(w, rcp);
+#pragma unroll
+    for (int k = 0; k < kQuantUnroll; ++k) {
+      const int64_t v = v0 + k * nthr;
+      const u32x2_t codes = quantize8_bf16_e4m3(w[k], rcp);   // (all lanes: it holds a wave ballot)
+      if (v < nvec) __builtin_nontemporal_store(codes, reinterpret_cast<u32x2_t*>(out + v * 8));
+    }
   }
 }
 
@@ -49,8 +70,8 @@ hipError_t launch_quantize_q(const void* q, int64_t ntok, int32_t nheads, int32_
   const int32_t vph = d / 8;
   const int64_t nvec = ntok * nheads * vph;
   if (nvec == 0) return hipSuccess;
-  int64_t blocks = (nvec + 255) / 256;
-  if (blocks > 256 * 64) blocks = 256 * 64;
+  int64_t blocks = (nvec + 256 * kQuantUnroll - 1) / (256 * kQuantUnroll);
+  if (blocks > (1 << 30)) blocks = 1 << 30;   // beyond that, the grid-stride loop takes the rest
   const bool contig = stride_head == d && stride_tok == (int64_t)nheads * d;
   if (contig)
     hipLaunchKernelGGL(quantize_q_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,

@@ -54,6 +54,26 @@ def test_quantize_q_strided_input():
     assert np.array_equal(got, ref)
 
 
+def test_quantize_q_large_ragged():
+    """A 1 GB-class Q whose vector count leaves the last block ragged: 16,411 tokens x 31 heads x
+    256 are 16,279,712 16-byte vectors, not a multiple of the 512 a block takes.  Sampled
+    positions and the last 300,000 elements (the ragged block and the full blocks before it) are
+    compared bit for bit with the oracle."""
+    fa = _fa()
+    g = torch.Generator(device="cuda").manual_seed(21)
+    q = torch.randn((16411, 31, 256), generator=g, device="cuda").to(torch.bfloat16)
+    ds32 = np.float32(q.float().abs().max().item() / 448.0)
+    ds = torch.tensor([ds32], dtype=torch.float32, device="cuda")
+    got = fa.fp8attn_quantize_q(q, ds).reshape(-1)
+    n = got.numel()
+    idx = torch.from_numpy(np.random.default_rng(3).choice(n, 1 << 21, replace=False)).cuda()
+    tail = torch.arange(n - 300_000, n, device="cuda")
+    for sel in (idx, tail):
+        x = q.reshape(-1)[sel].float().cpu().numpy()
+        ref = quantize_e4m3(x, ds32)
+        assert np.array_equal(got[sel].cpu().numpy(), ref)
+
+
 # ------------------------------------------------------------------------------------------
 # the tiny workload through both entry points and both query dtypes
 # ------------------------------------------------------------------------------------------

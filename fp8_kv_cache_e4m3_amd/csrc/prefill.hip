@@ -498,22 +498,60 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));       // nothing may land after the block ends
 
   // ---- epilogue ------------------------------------------------------------------------------
+  // O leaves through LDS.  Each wave writes its 32 normalized bf16 rows, in the accumulator
+  // layout, into its own part of the freed stage ring, and reads them back along the rows.  Every
+  // store instruction then writes whole row segments, 16 bytes per lane with consecutive lanes
+  // on consecutive bytes.  Stored straight from the accumulators, one instruction writes 8 bytes
+  // into each of 32 rows, and HBM took a third more bytes than O has.  The split-P instance
+  // (the first few hundred rows of each sequence) keeps the direct stores: it has no registers
+  // to spare for the staging.
   l_run += __shfl_xor(l_run, 32, 64);
-  if (!rvalid) return;
   const float inv = l_run > 0.f ? vd / l_run : 0.f;
-  __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)(t0 + tok) * p.out_stride_tok +
-               (int64_t)hq * p.out_stride_head;
+  if constexpr (!SPLIT) {
+    constexpr int ORS = 2 * D + 16;                 // LDS row stride of the staged O (bytes)
+    static_assert(S::NW * S::RW * ORS <= 4 * SB, "the staged O fits the stage ring");
+    __syncthreads();                                // every wave's loads have landed and its reads are done
+    uint8_t* const ow = lds + wave * (S::RW * ORS);
 #pragma unroll
-  for (int dt = 0; dt < S::NDT; ++dt) {
+    for (int dt = 0; dt < S::NDT; ++dt) {
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d = 16 * dt + (i4 >= 2 ? D / 2 : 0) + 8 * (i4 & 1) + 4 * lg;
-      const bf16x4_t o = {(__bf16)(oacc[dt][4 * i4] * inv), (__bf16)(oacc[dt][4 * i4 + 1] * inv),
-                          (__bf16)(oacc[dt][4 * i4 + 2] * inv), (__bf16)(oacc[dt][4 * i4 + 3] * inv)};
-      *reinterpret_cast<bf16x4_t*>(op + d) = o;
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 16 * dt + (i4 >= 2 ? D / 2 : 0) + 8 * (i4 & 1) + 4 * lg;
+        const bf16x4_t o = {(__bf16)(oacc[dt][4 * i4] * inv), (__bf16)(oacc[dt][4 * i4 + 1] * inv),
+                            (__bf16)(oacc[dt][4 * i4 + 2] * inv), (__bf16)(oacc[dt][4 * i4 + 3] * inv)};
+        *reinterpret_cast<bf16x4_t*>(ow + lr * ORS + 2 * d) = o;
+      }
+    }
+    // (a wave reads back only the rows it wrote: its own LDS accesses stay in program order)
+    constexpr int CPR = D / 8;                      // 16-byte chunks per row
+    __bf16* const obase = reinterpret_cast<__bf16*>(p.out);
+#pragma unroll
+    for (int k = 0; k < S::RW * CPR / 64; ++k) {
+      const int c = 64 * k + lane;
+      const int row = c / CPR, col = c % CPR;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ow + row * ORS + 16 * col);
+      const int rr = wr0 + row;
+      if (rr < nrows) {
+        const int tk = rr / G, hh = h * G + rr % G;
+        *reinterpret_cast<u32x4_t*>(obase + (int64_t)(t0 + tk) * p.out_stride_tok +
+                                    (int64_t)hh * p.out_stride_head + 8 * col) = v;
+      }
+    }
+  } else if (rvalid) {
+    __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)(t0 + tok) * p.out_stride_tok +
+                 (int64_t)hq * p.out_stride_head;
+#pragma unroll
+    for (int dt = 0; dt < S::NDT; ++dt) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 16 * dt + (i4 >= 2 ? D / 2 : 0) + 8 * (i4 & 1) + 4 * lg;
+        const bf16x4_t o = {(__bf16)(oacc[dt][4 * i4] * inv), (__bf16)(oacc[dt][4 * i4 + 1] * inv),
+                            (__bf16)(oacc[dt][4 * i4 + 2] * inv), (__bf16)(oacc[dt][4 * i4 + 3] * inv)};
+        *reinterpret_cast<bf16x4_t*>(op + d) = o;
+      }
     }
   }
-  if (p.lse && lg == 0)
+  if (p.lse && lg == 0 && rvalid)
     p.lse[(int64_t)(t0 + tok) * p.hq + hq] = l_run > 0.f ? (m_used + fast_log2(l_run)) * kLn2 : kNegInf;
 }
 

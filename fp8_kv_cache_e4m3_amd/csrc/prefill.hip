@@ -569,9 +569,13 @@ hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, bool q_bf16, hi
   const int G = p.group;
   const int64_t nqb = ((int64_t)p.max_seqlen_q * G + 255) / 256;
   if (nqb <= 0 || p.hkv <= 0 || p.batch <= 0) return hipSuccess;
-  // A block runs in the split-P instance iff its first row sees fewer than kSplitPKeys keys, which
-  // needs its first row's token index below kSplitPKeys: only q blocks qb < nqb_split can.
-  const int64_t nqb_split = std::min<int64_t>(nqb, ((int64_t)(kSplitPKeys - 1) * G) / 256 + 1);
+  // A block runs in the split-P instance iff its first row sees fewer than kSplitPKeys keys:
+  // min(position + 1, window).  A window shorter than kSplitPKeys puts every block there.
+  // Otherwise the first row's token index must be below kSplitPKeys, so only q blocks
+  // qb < nqb_split can.
+  const bool short_window = p.window >= 1 && p.window < kSplitPKeys;
+  const int64_t nqb_split =
+      short_window ? nqb : std::min<int64_t>(nqb, ((int64_t)(kSplitPKeys - 1) * G) / 256 + 1);
   const int64_t grid = nqb * p.hkv * p.batch, grid_split = nqb_split * p.hkv * p.batch;
   if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidConfiguration;
   if (head_dim == 256) {

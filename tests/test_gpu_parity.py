@@ -377,6 +377,20 @@ def test_split_q_row_scales():
     assert np.all(np.abs(l - l_ref) <= 1e-2 + 1e-4 * np.abs(l_ref)), np.max(np.abs(l - l_ref) / (1 + np.abs(l_ref)))
 
 
+@pytest.mark.parametrize("d,q_dtype,fused", [(64, "e4m3", False), (256, "e4m3", False), (256, "e4m3", True)])
+def test_prefill_short_window_long_sequence(d, q_dtype, fused):
+    """FP8 prefill with a window shorter than the split-P threshold over a sequence long enough
+    that most q blocks lie past the first few: every block belongs to the split-P instance, whose
+    grid must then cover all of them (every row of the output is compared)."""
+    w = wl.custom(q_dtype, d, 4, 2, 100, [1500, 700], [1500, 300], seed=31)
+    log(f"[case] short window prefill d{d} fused={fused} W=100 lens={w.seqlens_k_host} q={w.q_lens_host}")
+    o_ref, l_ref, codes_ref = oracle_run(w)
+    o, l, codes, _ = gpu_run(w, "prefill", fused_q=fused)
+    if codes is not None:
+        assert np.array_equal(codes, codes_ref)
+    compare(o, o_ref, l, l_ref, label=f"short window prefill d{d} fused={fused}")
+
+
 def test_page_size_128_and_strided_output():
     """Framework blocks of 128 tokens (two kernel pages) and an output with padded strides."""
     fa = _fa()

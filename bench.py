@@ -395,7 +395,7 @@ def main():
     args = ap.parse_args()
     fused = not args.separate_quantize
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
@@ -446,6 +446,8 @@ def main():
             ("full_decode", lambda s: wl.full_decode(device="cuda", seed=200 + s), "decode", 4, "hbm", False),
             ("spec_verify", lambda s: wl.spec_verify(device="cuda", seed=300 + s), "decode", 2, "hbm", False),
             ("swa_prefill", lambda s: wl.swa_prefill(device="cuda", seed=400 + s), "prefill", 2, "mfma", False),
+            # the same prefill on E4M3 codes quantized by a separate call: the attention kernel alone
+            ("swa_prefill_codes", lambda s: wl.swa_prefill(device="cuda", seed=400 + s), "prefill", 2, "mfma", False),
             # the same bf16-Q workloads with QK^T on the FP8 MFMA (split Q)
             ("full_decode_split_q", lambda s: wl.full_decode(device="cuda", seed=200 + s), "decode", 4, "hbm", True),
             ("spec_verify_split_q", lambda s: wl.spec_verify(device="cuda", seed=300 + s), "decode", 2, "hbm", True),
@@ -455,19 +457,22 @@ def main():
              True),
         ]
         for name, make, entry, ns, bound, split in specs:
-            r = time_workload(make, entry, ns, max(5, args.steps // 5), 2, name, fused, split)
+            fz = fused and not name.endswith("_codes")
+            r = time_workload(make, entry, ns, max(5, args.steps // 5), 2, name, fz, split)
             ww = r["w"]
-            tb, kvb = algo_bytes(ww, fused)
+            tb, kvb = algo_bytes(ww, fz)
             fl = algo_flops(ww)
             e = {"workload": ww.name, "ms_per_step": round(r["ms_per_step"], 4),
                  "attention_ms": round(r["kernel_ms"], 4), "splits": r["splits"],
                  "kv_read_GBps": round(tb / (r["kernel_ms"] * 1e-3) / 1e9, 1),
                  "TFLOPs": round(fl / (r["kernel_ms"] * 1e-3) / 1e12, 2)}
+            if not fz and ww.q_dtype == "e4m3":
+                e["step"] = "quantize_q, then the attention call on E4M3 codes (attention_ms: that call alone)"
             # HBM bytes of the step's kernels (decode plus the partition's combine; both prefill instances)
             keys = {"full_decode": ["decode_full", "decode_full_combine"], "spec_verify": ["decode_spec"],
                     "swa_prefill": ["prefill_swa", "prefill_swa_splitp"]}.get(name)
             tr = [load_traffic(k) for k in keys] if keys else [None]
-            e["traffic"] = sum(tr) if fused and all(t is not None for t in tr) else None
+            e["traffic"] = sum(tr) if fz and all(t is not None for t in tr) else None
             if bound == "hbm":
                 e["hbm_frac"] = round(e["kv_read_GBps"] / HBM_PEAK_GBS, 4)
             else:

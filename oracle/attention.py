@@ -80,10 +80,18 @@ def visible_mask(q_positions, key_positions, window: int):
     return m
 
 
-def _descale(x):
+def descale_at(x, b: int, h: int) -> float:
+    """The fp32 descale of sequence b and kv head h.  ``x`` is None (1.0), one per-tensor value
+    (a scalar or one-element array), or a [B, Hkv] array of per-(sequence, kv head) values, the
+    layout the pages forward to the kernel (prhub digest of vLLM PR #48666, Key code: descales
+    expanded to (batch, num_kv_heads))."""
     if x is None:
         return 1.0
-    return float(np.float32(_np(x).reshape(-1)[0]))
+    a = _np(x)
+    if a.size == 1:
+        return float(np.float32(a.reshape(-1)[0]))
+    assert a.ndim == 2, "per-(sequence, kv head) descales are a [B, Hkv] array"
+    return float(np.float32(a[b, h]))
 
 
 def paged_attention(q_vals, k_pool, v_pool, block_table, cu_seqlens_q, seqlens_k,
@@ -97,6 +105,8 @@ def paged_attention(q_vals, k_pool, v_pool, block_table, cu_seqlens_q, seqlens_k
     returns  : (o [total_q, Hq, d], lse [total_q, Hq]), both fp64.  Rows not
                selected by ``tokens`` (an optional list of global query-token
                indices) are NaN.
+    k_descale, v_descale: None (1.0), one per-tensor value, or [B, Hkv] arrays of
+               per-(sequence, kv head) values (see descale_at).
     key_ranges: optional [B] list of (k_lo, k_hi) that further limits the keys
                to lo <= j < hi.  This is the attention of one KV split.  A row
                with no visible key then gets o = 0 and lse = -inf, which is the
@@ -112,7 +122,6 @@ def paged_attention(q_vals, k_pool, v_pool, block_table, cu_seqlens_q, seqlens_k
     hkv = num_kv_heads
     assert hq % hkv == 0
     g = hq // hkv
-    kd, vd = _descale(k_descale), _descale(v_descale)
     out = np.full((total_q, hq, d), np.nan)
     lse = np.full((total_q, hq), np.nan)
     sel = None if tokens is None else set(int(t) for t in tokens)
@@ -137,6 +146,7 @@ def paged_attention(q_vals, k_pool, v_pool, block_table, cu_seqlens_q, seqlens_k
             kc = gather_pages(k_pool, bt[b], keys, page_size)  # [nk, Hkv, d]
             vc = gather_pages(v_pool, bt[b], keys, page_size)
             for h in range(hkv):
+                kd, vd = descale_at(k_descale, b, h), descale_at(v_descale, b, h)
                 K = E4M3_TABLE[kc[:, h, :]] * kd              # [nk, d] fp64
                 V = E4M3_TABLE[vc[:, h, :]] * vd
                 Q = q_vals[ct, h * g:(h + 1) * g, :]           # [n, g, d]

@@ -27,7 +27,8 @@ def _decode(code: int) -> float:
 def brute_attention(q_vals, k_pool, v_pool, block_table, cu_seqlens_q, seqlens_k,
                     num_kv_heads, softmax_scale, window, k_descale, v_descale, page_size):
     """q_vals: nested lists [total_q][Hq][d] of floats; pools: nested lists [pages][page_size][Hkv][d]
-    of ints (codes); returns (o, lse) as nested lists."""
+    of ints (codes); k_descale / v_descale: one float, or nested lists [B][Hkv] (one value per
+    sequence and kv head); returns (o, lse) as nested lists."""
     total_q = len(q_vals)
     hq = len(q_vals[0])
     d = len(q_vals[0][0])
@@ -52,13 +53,15 @@ def brute_attention(q_vals, k_pool, v_pool, block_table, cu_seqlens_q, seqlens_k
             t = t0 + i
             for h in range(hq):
                 kvh = h // g
+                kds = k_descale[b][kvh] if isinstance(k_descale, (list, tuple)) else k_descale
+                vds = v_descale[b][kvh] if isinstance(v_descale, (list, tuple)) else v_descale
                 scores = []
                 for j in range(L):
                     if not mask[i][j]:
                         continue
                     page = int(block_table[b][j // page_size])
                     slot = j % page_size
-                    kr = [_decode(int(c)) * k_descale for c in k_pool[page][slot][kvh]]
+                    kr = [_decode(int(c)) * kds for c in k_pool[page][slot][kvh]]
                     s = softmax_scale * math.fsum(q_vals[t][h][x] * kr[x] for x in range(d))
                     scores.append((j, s))
                 m = max(s for _, s in scores)
@@ -69,15 +72,8 @@ def brute_attention(q_vals, k_pool, v_pool, block_table, cu_seqlens_q, seqlens_k
                     for j, e in w:
                         page = int(block_table[b][j // page_size])
                         slot = j % page_size
-                        acc.append(e * _decode(int(v_pool[page][slot][kvh][x])) * v_descale)
+                        acc.append(e * _decode(int(v_pool[page][slot][kvh][x])) * vds)
                     o[t][h][x] = math.fsum(acc) / l
                 lse[t][h] = m + math.log(l)
     return o, lse
 
-
-def brute_softmax_rows(scores):
-    """Softmax of one list of scores with math.exp / math.fsum (used for the row-sum invariant)."""
-    m = max(scores)
-    e = [math.exp(s - m) for s in scores]
-    l = math.fsum(e)
-    return [x / l for x in e]

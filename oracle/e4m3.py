@@ -9,6 +9,12 @@ spell out the rounding.  The reading adopted here is IEEE fp32 division by the
 descale, then round-to-nearest-even with saturation at +-448.  A NaN keeps its
 sign as code 0x7F | sign.  This module implements exactly that rule and nothing
 faster.
+
+The sign of every code is the sign IEEE division gives the quotient: sign(x)
+XOR sign(descale).  That includes a NaN quotient, so 0 / 0 (an all-zero tensor
+gets descale amax / 448 = 0) gives 0x7F for +0 and 0xFF for -0.  (IEEE leaves
+the sign of a NaN that an invalid operation creates to the platform; numpy on
+x86 makes it negative.  The rule here fixes it to the sign of the operands.)
 """
 from __future__ import annotations
 
@@ -51,19 +57,20 @@ def quantize_e4m3(x, descale=1.0) -> np.ndarray:
 
     Steps:
       1. y = float32(x) / float32(descale), one IEEE binary32 division (RNE).
-      2. NaN gives 0x7F with y's sign bit.
+      2. NaN gives 0x7F with the quotient's sign.
       3. |y| >= 448 (including inf) saturates to 0x7E with y's sign.
       4. Otherwise pick the E4M3 magnitude nearest to |y|, comparing in fp64.
          Both operands are exact there, so the comparison is exact.  A tie goes
-         to the even code, i.e. the even mantissa.  The sign is y's sign bit,
-         so -0 gives 0x80.
+         to the even code, i.e. the even mantissa.  -0 gives 0x80.
+    The quotient's sign is sign(x) XOR sign(descale), the IEEE rule for
+    division, taken for NaN quotients too (see the module docstring).
     """
     x32 = np.asarray(x, dtype=np.float32)
     d32 = np.float32(descale)
     with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
         y = (x32 / d32).astype(np.float32)
     a = np.abs(y.astype(np.float64))
-    sign = np.where(np.signbit(y), 0x80, 0x00).astype(np.uint8)
+    sign = np.where(np.signbit(x32) ^ np.signbit(d32), 0x80, 0x00).astype(np.uint8)
     nan = np.isnan(a)
     a_f = np.where(nan, 0.0, a)
     hi = np.clip(np.searchsorted(_POS, a_f, side="left"), 0, 126)   # _POS[hi] >= a (or 126)

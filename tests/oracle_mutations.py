@@ -42,6 +42,10 @@ MUTATIONS = {
     "subnormal_exponent": ("e4m3.py", "        return s * (m / 8.0) * 2.0 ** -6", "        return s * (m / 8.0) * 2.0 ** -7"),
     "saturation_to_nan": ("e4m3.py", "    mag = np.where(a_f >= E4M3_MAX, 0x7E, mag)",
                           "    mag = np.where(a_f >= E4M3_MAX, 0x7F, mag)"),
+    "nan_sign_from_platform": ("e4m3.py", "np.signbit(x32) ^ np.signbit(d32)", "np.signbit(y)"),
+    "default_scale_one_over_d": ("attention.py", "    return 1.0 / math.sqrt(head_dim)", "    return 1.0 / head_dim"),
+    "descale_per_head_transposed": ("attention.py", "    return float(np.float32(a[b, h]))",
+                                    "    return float(np.float32(a.reshape(-1)[h * a.shape[0] + b]))"),
     "cache_page_slot_swapped": ("cache_write.py", "        page, pos = divmod(slot, page_size)",
                                 "        pos, page = divmod(slot, page_size)"),
     "cache_descale_swapped": ("cache_write.py", "        vc[page, pos] = quantize_e4m3(v_new[t], v_descale)",

@@ -258,3 +258,35 @@ def test_token_subset_equals_full_rows():
     for t in [1, 6, 9]:
         assert np.array_equal(o0[t], o1[t]) and np.array_equal(l0[t], l1[t])
     assert np.isnan(o1[0]).all()
+
+
+def test_default_scale_closed_form():
+    """The softmax scale the pages leave open is read as 1/sqrt(head_dim): exact powers of two at
+    the even-power head dims, 2^-4.5 at 512 and a value whose square is 1/96 at 96."""
+    assert default_scale(256) == 0.0625
+    assert default_scale(64) == 0.125
+    assert default_scale(16) == 0.25
+    assert abs(default_scale(512) - 2.0 ** -4.5) < 1e-17          # 1/sqrt(512) = 2^-4.5
+    assert abs(default_scale(96) * default_scale(96) * 96 - 1.0) < 1e-15
+
+
+def test_per_sequence_head_descales_match_brute_force():
+    """K/V descales laid out per (sequence, kv head): the oracle's lookup against the brute force,
+    which reads its own nested lists [B][Hkv]."""
+    w = _small("bf16", hq=4, hkv=2, seqlens=(70, 3, 130), qlens=(5, 3, 2), seed=4)
+    kd = np.array([[0.5, 2.0], [1.25, 0.75], [3.0, 0.125]], dtype=np.float32) * float(w.k_descale[0])
+    vd = np.array([[1.5, 0.25], [2.0, 1.0], [0.5, 4.0]], dtype=np.float32) * float(w.v_descale[0])
+    qv, _ = query_values(w.q, "bf16")
+    o, l = paged_attention(qv, w.k_pool, w.v_pool, w.block_table, w.cu_seqlens_q, w.seqlens_k, 2,
+                           default_scale(w.head_dim), -1, kd, vd)
+    ob, lb = brute.brute_attention(qv.tolist(), w.k_pool.numpy().tolist(), w.v_pool.numpy().tolist(),
+                                   w.block_table.numpy().tolist(), w.cu_seqlens_q.numpy().tolist(),
+                                   w.seqlens_k.numpy().tolist(), 2, default_scale(w.head_dim), -1,
+                                   kd.astype(np.float64).tolist(), vd.astype(np.float64).tolist(), 64)
+    assert np.max(np.abs(o - np.array(ob))) < 1e-12 and np.max(np.abs(l - np.array(lb))) < 1e-12
+    # and the per-tensor case is the (b, h) case with every entry equal
+    o1, l1 = _run(w)
+    full = np.full((3, 2), np.float32(w.k_descale[0])), np.full((3, 2), np.float32(w.v_descale[0]))
+    o2, l2 = paged_attention(qv, w.k_pool, w.v_pool, w.block_table, w.cu_seqlens_q, w.seqlens_k, 2,
+                             default_scale(w.head_dim), -1, *full)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

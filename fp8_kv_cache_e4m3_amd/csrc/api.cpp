@@ -98,8 +98,12 @@ fp8attn_status validate_attn(const char* fn, const fp8attn_attn_args* a, bool de
                 "%s: non-causal attention is not supported (q=%s k=e4m3 v=e4m3 head_size=%d): only causal "
                 "and sliding-window masks are implemented",
                 fn, dtype_name(a->q_dtype), a->head_dim);
-  if (a->window == 0 || a->window < -1)
+  if (a->window < -1)
     return fail(FP8ATTN_ERR_INVALID_ARG, "%s: window must be -1 (none) or >= 1, got %d", fn, a->window);
+  if (a->window == 0)
+    return fail(FP8ATTN_ERR_UNSUPPORTED,
+                "%s: window 0 (no visible key) is not supported (q=%s k=e4m3 v=e4m3 head_size=%d): window must be "
+                "-1 (none) or >= 1", fn, dtype_name(a->q_dtype), a->head_dim);
   if (a->page_size <= 0 || a->page_size % 64 != 0)
     return fail(FP8ATTN_ERR_UNSUPPORTED,
                 "%s: page_size %d is not a positive multiple of 64 (q=%s k=e4m3 v=e4m3 head_size=%d)", fn,
@@ -135,6 +139,10 @@ fp8attn_status validate_attn(const char* fn, const fp8attn_attn_args* a, bool de
       a->kv_stride_head < 0 || a->kv_stride_page < 0)
     return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: k/v caches must be 16-byte aligned with 16-byte-multiple strides "
                 "(kv_stride_tok >= head_dim)", fn);
+  // the kernels address the keys of one 64-key tile with 32-bit byte offsets from its first key
+  if (a->kv_stride_tok > (int64_t)(UINT32_MAX / 64))
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: kv_stride_tok %lld is too large: 64 token strides must stay below 2^32 "
+                "bytes", fn, (long long)a->kv_stride_tok);
   if (!aligned(a->out, 16) || (a->out_stride_tok * 2) % 16 != 0 || (a->out_stride_head * 2) % 16 != 0 ||
       a->out_stride_tok < 0 || a->out_stride_head < 0)
     return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: out must be 16-byte aligned with 16-byte-multiple strides", fn);

@@ -55,11 +55,26 @@ struct UnitRegs {
   uint32_t v[4][DecodeShape<D>::VBLK][DecodeShape<D>::CW / 4];
 };
 
-// K/V byte loads; NT marks them non-temporal (streamed once, no reuse).
-template <bool NT, class T>
-__device__ __forceinline__ T stream_load(const T* p) {
-  if constexpr (NT) return __builtin_nontemporal_load(p);
-  else return *p;
+// K/V byte loads through a buffer resource whose range ends after the unit's last key below the
+// sequence length: lanes addressing keys at or past it read zeros (out-of-range buffer loads).
+// Those slots are never written for this sequence and may hold any bytes, E4M3 NaN codes
+// included; their keys are masked (P = 0), but 0 * NaN is NaN in the MFMA.  NT marks the loads
+// non-temporal (streamed once, no reuse).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t unit_rsrc(const uint8_t* base, uint32_t num_records) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)num_records, 0x00020000);
+}
+template <bool NT>
+__device__ __forceinline__ u32x4_t stream_load16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0);
+}
+template <bool NT>
+__device__ __forceinline__ u32x2_t stream_load8(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, NT ? 2 : 0);
+}
+template <bool NT>
+__device__ __forceinline__ uint32_t stream_load4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, NT ? 2 : 0);
 }
 
 // Per-lane byte offsets inside a unit, the same for every unit: K row col, bytes 16 grp (+ 64 c);
@@ -74,14 +89,13 @@ struct UnitOffsets {
 // bytes lie past DV (k_hi_ok false: the last K chunk; v_ok false: the V columns) load nothing
 // and hold zeros, so no byte outside the head is read and the padding adds nothing.
 template <int D, int DV, bool NT>
-__device__ __forceinline__ void load_unit(UnitRegs<D>& ur, const uint8_t* __restrict__ kunit,
-                                          const uint8_t* __restrict__ vunit, const UnitOffsets& off,
-                                          const bool k_hi_ok, const bool v_ok) {
+__device__ __forceinline__ void load_unit(UnitRegs<D>& ur, const rsrc_t kunit, const rsrc_t vunit,
+                                          const UnitOffsets& off, const bool k_hi_ok, const bool v_ok) {
   using S = DecodeShape<D>;
 #pragma unroll
   for (int c = 0; c < S::KCH; ++c) {
     if (DV == D || c < S::KCH - 1 || k_hi_ok)
-      ur.k[c] = stream_load<NT>(reinterpret_cast<const u32x4_t*>(kunit + off.k + 64 * c));
+      ur.k[c] = stream_load16<NT>(kunit, off.k + 64 * c);
     else
       ur.k[c] = u32x4_t{0, 0, 0, 0};
   }
@@ -94,21 +108,20 @@ __device__ __forceinline__ void load_unit(UnitRegs<D>& ur, const uint8_t* __rest
         for (int x = 0; x < S::CW / 4; ++x) ur.v[i][blk][x] = 0u;
         continue;
       }
-      const uint8_t* vp = vunit + off.v[i] + blk * 16 * S::CW;
+      const uint32_t vo = off.v[i] + blk * 16 * S::CW;
       if constexpr (S::CW == 16) {
-        const u32x4_t w = stream_load<NT>(reinterpret_cast<const u32x4_t*>(vp));
+        const u32x4_t w = stream_load16<NT>(vunit, vo);
         ur.v[i][blk][0] = w[0];
         ur.v[i][blk][1] = w[1];
         ur.v[i][blk][2] = w[2];
         ur.v[i][blk][3] = w[3];
       } else if constexpr (S::CW == 8) {
-        const u32x2_t w = stream_load<NT>(reinterpret_cast<const u32x2_t*>(vp));
+        const u32x2_t w = stream_load8<NT>(vunit, vo);
         ur.v[i][blk][0] = w[0];
         ur.v[i][blk][1] = w[1];
       } else {   // 4 or 12 bytes: dword loads
 #pragma unroll
-        for (int x = 0; x < S::CW / 4; ++x)
-          ur.v[i][blk][x] = stream_load<NT>(reinterpret_cast<const uint32_t*>(vp + 4 * x));
+        for (int x = 0; x < S::CW / 4; ++x) ur.v[i][blk][x] = stream_load4<NT>(vunit, vo + 4 * x);
       }
     }
   }
@@ -346,11 +359,13 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
     const bool trailing = u > ulast;
     const int uc = trailing ? ulast : u;
     const int64_t unit = page_of(uc) * sP + (int64_t)((uc * 16) % ps) * sT;
+    // the unit's keys below L (at least one: uc * 16 <= p_last < L)
+    const uint32_t nrec = (uint32_t)min(16, L - uc * 16) * (uint32_t)sT;
     UnitOffsets o = uoff;
     o.k = trailing ? 0u : o.k;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o.v[i] = trailing ? 0u : o.v[i];
-    load_unit<DP, D, T::NT>(ur, kbase + unit, vbase + unit, o, k_hi_ok, v_ok);
+    load_unit<DP, D, T::NT>(ur, unit_rsrc(kbase + unit, nrec), unit_rsrc(vbase + unit, nrec), o, k_hi_ok, v_ok);
   };
 
   // S^T tile of a unit: rows = its 16 keys, columns = the 16 query rows

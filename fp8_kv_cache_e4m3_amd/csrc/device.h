@@ -15,6 +15,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector memory operations of
 // this wave are outstanding and leaves the other counters unconstrained
@@ -59,7 +60,23 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* gbase, uint32_t voff, u
                : "v"(voff), "s"(gbase), "s"(lds_dst)
                : "memory", "m0");
 }
+// The same copy through a buffer resource (V#): base address, no stride, num_records bytes.  A
+// lane whose offset lies at or past num_records is out of range and, as for every buffer load,
+// reads zeros, which land in LDS like any other data.
+__device__ __forceinline__ void lds_dma16_buf(const i32x4_t rsrc, uint32_t voff, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_dst)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// Raw buffer resource for the loads above: 48-bit base, stride 0 (offsets are plain byte offsets),
+// num_records bytes in range, and the gfx9 dword-3 word for untyped 32-bit accesses.
+__device__ __forceinline__ i32x4_t buffer_rsrc(const uint8_t* base, uint32_t num_records) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4_t{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)num_records, 0x00020000};
+}
 
 // ---------------------------------------------------------------------------------------------
 // E4M3 -> bf16, exact: every E4M3 value is a bf16 value.  gfx950's v_cvt_scalef32_pk_bf16_fp8
@@ -103,19 +120,21 @@ __device__ __forceinline__ void transpose4x4_u8(uint32_t a0, uint32_t a1, uint32
 // ---------------------------------------------------------------------------------------------
 // Q quantization to E4M3, shared by fp8attn_quantize_q and the attention kernels that take bf16
 // Q for the native-FP8 path (both give identical codes).  The rule: fp32 quotient q / descale,
-// round to nearest even, saturate at +-448, NaN -> 0x7F | sign.  The fp32 quotient is
+// round to nearest even, saturate at +-448; a NaN quotient gives 0x7F with the quotient's sign,
+// which IEEE division takes as sign(x) XOR sign(descale) also when the quotient is NaN (an input
+// NaN, or 0 / 0 and inf / inf with a zero or infinite descale).  The fp32 quotient is
 // RN32(RN64(x * RN64(1 / descale))), which equals the correctly rounded division for every x
 // with at most 24 significant bits; the argument is given where fp8attn_quantize_q is defined.
-// rcp is RN64(1 / descale).
+// rcp is RN64(1 / descale) and carries the descale's sign (1 / +-0 = +-inf).
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ float q_quotient_clamped(float x, double rcp) {
-  const float q = (float)((double)x * rcp);
+__device__ __forceinline__ float q_quotient(float x, double rcp) { return (float)((double)x * rcp); }
+__device__ __forceinline__ float clamp448(float q) {
   return __builtin_fminf(__builtin_fmaxf(q, -448.0f), 448.0f);   // a NaN is fixed afterwards
 }
 // the 8 bf16 of a 16-byte word -> 8 E4M3 codes (element i in byte i of the two dwords).
-// The clamp maps a NaN quotient to a finite value, so NaN inputs are patched afterwards.  The test
-// for them is a wave-wide ballot (one compare per element, OR-ed in scalar registers), and the
-// patch is a wave-uniform branch that real data never takes.
+// The clamp maps a NaN quotient to a finite value, so NaN quotients are patched afterwards.  The
+// test for them is a wave-wide ballot (one compare per element, OR-ed in scalar registers), and
+// the patch is a wave-uniform branch that real data never takes.
 __device__ __forceinline__ u32x2_t quantize8_bf16_e4m3(const u32x4_t w, double rcp) {
   float x[8], y[8];
   uint64_t nan_lanes = 0;
@@ -126,18 +145,21 @@ __device__ __forceinline__ u32x2_t quantize8_bf16_e4m3(const u32x4_t w, double r
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    y[k] = q_quotient_clamped(x[k], rcp);
-    nan_lanes |= __builtin_amdgcn_ballot_w64(x[k] != x[k]);
+    const float q = q_quotient(x[k], rcp);
+    nan_lanes |= __builtin_amdgcn_ballot_w64(q != q);
+    y[k] = clamp448(q);
   }
   int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
   lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
   int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
   hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
   if (nan_lanes != 0) {
+    const uint32_t ds_sign = (uint32_t)((uint64_t)__double_as_longlong(rcp) >> 56) & 0x80u;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      if (x[k] != x[k]) {
-        const uint32_t code = 0x7fu | ((__float_as_uint(x[k]) >> 24) & 0x80u);
+      const float q = q_quotient(x[k], rcp);
+      if (q != q) {
+        const uint32_t code = 0x7fu | (((__float_as_uint(x[k]) >> 24) & 0x80u) ^ ds_sign);
         const int sh = 8 * (k & 3);
         if (k < 4) lo = (int)(((uint32_t)lo & ~(0xffu << sh)) | (code << sh));
         else hi = (int)(((uint32_t)hi & ~(0xffu << sh)) | (code << sh));

@@ -100,9 +100,13 @@ struct PrefillShape {
 // per tile.  Wave w issues instructions w, w + 8, ...; every wave issues MAXI of them, a wave
 // that has one fewer repeating its previous one (the same bytes to the same place), so that the
 // issue is branch-free and every wave has the same number of loads in flight.
+// The loads go through buffer resources whose range ends after the tile's last key below the
+// sequence length: the rows of keys at or past it read zeros.  Those slots are never written for
+// this sequence and may hold any bytes, E4M3 NaN codes included; their keys are masked (P = 0),
+// but 0 * NaN is NaN in the MFMA, so their V rows must be finite, and zeros cost nothing here.
 struct TileLoad {
-  const uint8_t* k_src;   // K tile (page base plus the tile's first slot), uniform
-  const uint8_t* v_src;   // V tile
+  i32x4_t k_rsrc;         // K tile (page base plus the tile's first slot), uniform
+  i32x4_t v_rsrc;         // V tile
   uint32_t lds_stage;     // LDS address of the stage's [K tile | V tile]
 };
 template <int D>
@@ -120,8 +124,8 @@ __device__ __forceinline__ void tile_load_step(const TileLoad& tl, const uint32_
   const int ins = load_instruction<D>(wave, k);
   const int which = ins / S::SLOTS;
   const int blk = ins % S::SLOTS;
-  lds_dma16(which ? tl.v_src : tl.k_src, idle ? 0u : loff[k],
-            tl.lds_stage + (uint32_t)(which * S::TILE + blk * 1024));
+  lds_dma16_buf(which ? tl.v_rsrc : tl.k_rsrc, idle ? 0u : loff[k],
+                tl.lds_stage + (uint32_t)(which * S::TILE + blk * 1024));
 }
 
 // The MFMA work of one wave between two barriers: O^T += V^T * P^T for one tile (PV) and then
@@ -302,11 +306,14 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   auto page_id = [&](int kt) __attribute__((always_inline)) -> int {
     return bt[ps == S::BK ? kt : (kt * S::BK) / ps];
   };
-  // issue this wave's loads of tile kt (page id page) into the stage at byte offset so
+  // issue this wave's loads of tile kt (page id page) into the stage at byte offset so; the range
+  // of the tile's buffers ends with its last key below L (rows past it read zeros)
   auto issue = [&](int so, int kt, int page, bool idle = false) __attribute__((always_inline)) {
     const int slot0 = ps == S::BK ? 0 : kt * S::BK - ((kt * S::BK) / ps) * ps;
     const int64_t tile_off = (int64_t)page * sP + (int64_t)slot0 * sT;
-    const TileLoad tl{kbase + tile_off, vbase + tile_off, lds_base + (uint32_t)so};
+    const uint32_t nrec = (uint32_t)min(S::BK, L - kt * S::BK) * (uint32_t)sT;
+    const TileLoad tl{buffer_rsrc(kbase + tile_off, nrec), buffer_rsrc(vbase + tile_off, nrec),
+                      lds_base + (uint32_t)so};
 #pragma unroll
     for (int k = 0; k < S::MAXI; ++k) tile_load_step<D>(tl, loff, wave, k, idle);
   };

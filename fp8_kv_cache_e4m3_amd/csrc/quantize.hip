@@ -10,9 +10,10 @@
 // difference x - m * descale, for a halfway point m, is a nonzero multiple of a power of two
 // that small relative to x.  So the single rounding to fp32 lands where the correctly rounded
 // division does.  The E4M3 rounding then uses the converter (round to nearest even) on the
-// value clamped to +-448, which is the saturation of the rule.  The converter turns every NaN into
-// 0xFF, whereas the rule keeps the sign (0x7F | sign): a branch taken only where a lane holds a
-// NaN writes those codes.
+// value clamped to +-448, which is the saturation of the rule.  The clamp turns a NaN quotient
+// (a NaN input, or 0 / 0 with a zero descale) into a finite value, whereas the rule gives
+// 0x7F | sign with the quotient's IEEE sign, sign(x) XOR sign(descale): a branch taken only where
+// a lane's quotient is NaN writes those codes.
 #include "device.h"
 #include "params.h"
 

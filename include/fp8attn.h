@@ -116,7 +116,8 @@ typedef struct fp8attn_attn_args {
 
   float softmax_scale;              /* <= 0 selects 1/sqrt(head_dim) */
   int32_t causal;                   /* must be 1: causal and local masks only ([60372]) */
-  int32_t window;                   /* -1: none.  W >= 1: keys p-W < j <= p.  0 is rejected */
+  int32_t window;                   /* -1: none.  W >= 1: keys p-W < j <= p.  0 (a window that
+                                       shows no key) is FP8ATTN_ERR_UNSUPPORTED; < -1 INVALID_ARG */
 
   void* out;                        /* bf16 [total_q, num_q_heads, head_dim], d contiguous */
   int64_t out_stride_tok, out_stride_head;

@@ -85,8 +85,12 @@ def gpu_run(w: wl.Workload, entry="decode", num_splits=0, window=None, softmax_s
         q, qd = wd.q, None
     win = w.window if window is None else window
     assert not split_q or w.q_dtype == "bf16", "split Q takes bf16 queries"
+    # K/V descales: one per-tensor value, or [B, Hkv] per (sequence, kv head)
+    ds_strides = (0, 0) if wd.k_descale.numel() == 1 else (wd.k_descale.stride(0), wd.k_descale.stride(1))
+    assert wd.v_descale.numel() == wd.k_descale.numel(), "K and V descales share one layout"
     kw = dict(q_descale=qd, k_descale=wd.k_descale, v_descale=wd.v_descale, softmax_scale=softmax_scale,
-              window=win, want_lse=want_lse, out=out, quantize_q=fused_q, split_q=split_q)
+              window=win, want_lse=want_lse, out=out, quantize_q=fused_q, split_q=split_q,
+              descale_strides=ds_strides)
     args = (q, wd.k_pool, wd.v_pool, wd.block_table, wd.cu_seqlens_q, wd.seqlens_k, w.max_seqlen_q,
             w.max_seqlen_k)
     splits = 1
@@ -129,3 +133,64 @@ def sample_tokens(w: wl.Workload, n: int, seed: int = 0):
     extra = rng.choice(int(cu[-1]), size=min(n, int(cu[-1])), replace=False)
     picks.update(int(x) for x in extra)
     return sorted(picks)
+
+
+def with_page_size(w: wl.Workload, page_size: int, seed: int = 4) -> wl.Workload:
+    """The same logical K/V rows re-packed into framework blocks of page_size tokens (a multiple of
+    64), placed in a fresh seeded random order.  Slots past a sequence's length stay zero."""
+    import math as _m
+    k, v, bt = w.k_pool, w.v_pool, w.block_table
+    nblk = [_m.ceil(L / page_size) for L in w.seqlens_k_host]
+    perm = np.random.default_rng(seed).permutation(sum(nblk))
+    k2 = torch.zeros((sum(nblk), page_size) + tuple(k.shape[2:]), dtype=torch.uint8)
+    v2 = torch.zeros_like(k2)
+    table = torch.zeros((len(nblk), max(nblk)), dtype=torch.int32)
+    nxt = 0
+    for b, L in enumerate(w.seqlens_k_host):
+        for n in range(nblk[b]):
+            table[b, n] = int(perm[nxt])
+            nxt += 1
+        j = torch.arange(L)
+        src_pages = bt[b, j // 64].long()
+        dst_pages = table[b, j // page_size].long()
+        k2[dst_pages, j % page_size] = k[src_pages, j % 64]
+        v2[dst_pages, j % page_size] = v[src_pages, j % 64]
+    w2 = wl.Workload(**{**w.__dict__})
+    w2.k_pool, w2.v_pool, w2.block_table = k2, v2, table
+    return w2
+
+
+def with_nan_tails(w: wl.Workload) -> wl.Workload:
+    """A copy whose pool slots past each sequence's length, in its last page, hold the E4M3 NaN
+    codes (0x7F in K, 0xFF in V).  Those slots are never written for the sequence; no key there is
+    visible, so the outputs must not change."""
+    k, v = w.k_pool.clone(), w.v_pool.clone()
+    ps = k.shape[1]
+    for b, L in enumerate(w.seqlens_k_host):
+        last = (L - 1) // ps
+        page = int(w.block_table[b, last])
+        s0 = L - last * ps
+        if s0 < ps:
+            k[page, s0:] = 0x7F
+            v[page, s0:] = 0xFF
+    w2 = wl.Workload(**{**w.__dict__})
+    w2.k_pool, w2.v_pool = k, v
+    return w2
+
+
+def prefill_split_p_blocks(w: wl.Workload, rows_per_block: int = 256, split_p_keys: int = 512):
+    """Which q blocks of the FP8 prefill run the single-P instance and which the split-P one, from
+    the kernel's dispatch rule: a block of rows_per_block (token, q head) rows whose first row sees
+    fewer than split_p_keys keys, min(position + 1, window), takes split P.  Returns the counts
+    (single_p, split_p) over every (sequence, kv head, q block) that holds rows."""
+    G = w.num_q_heads // w.num_kv_heads
+    single = split = 0
+    for L, ql in zip(w.seqlens_k_host, w.q_lens_host):
+        for qb in range((ql * G + rows_per_block - 1) // rows_per_block):
+            pf = L - ql + (qb * rows_per_block) // G
+            keys = pf + 1 if w.window < 1 else min(pf + 1, w.window)
+            if keys < split_p_keys:
+                split += w.num_kv_heads
+            else:
+                single += w.num_kv_heads
+    return single, split

@@ -80,7 +80,7 @@ def _status(a, fn="prefill"):
     ({"q_dtype": fa.E4M3, "head_dim": 80}, fa.ERR_UNSUPPORTED, ["q=e4m3", "head_size=80"]),
     ({"page_size": 32}, fa.ERR_UNSUPPORTED, ["page_size 32", "multiple of 64"]),
     ({"page_size": 96}, fa.ERR_UNSUPPORTED, ["page_size 96"]),
-    ({"window": 0}, fa.ERR_INVALID_ARG, ["window"]),
+    ({"window": 0}, fa.ERR_UNSUPPORTED, ["window 0", "q=bf16", "head_size=512"]),
     ({"window": -2}, fa.ERR_INVALID_ARG, ["window"]),
     ({"num_q_heads": 7}, fa.ERR_INVALID_ARG, ["multiple of num_kv_heads"]),
     ({"num_kv_heads": 0}, fa.ERR_INVALID_ARG, ["positive"]),
@@ -90,6 +90,7 @@ def _status(a, fn="prefill"):
     ({"q": 0}, fa.ERR_INVALID_ARG, ["NULL"]),
     ({"out": 0}, fa.ERR_INVALID_ARG, ["NULL"]),
     ({"kv_stride_tok": 1000}, fa.ERR_UNSUPPORTED, ["16-byte"]),
+    ({"kv_stride_tok": 1 << 26}, fa.ERR_UNSUPPORTED, ["kv_stride_tok", "2^32"]),
     ({"q_stride_head": 100}, fa.ERR_UNSUPPORTED, ["q must be 16-byte"]),
     ({"softmax_scale": float("nan")}, fa.ERR_INVALID_ARG, ["softmax_scale"]),
     ({"block_table_stride": 1}, fa.ERR_INVALID_ARG, ["block_table_stride"]),
@@ -243,6 +244,6 @@ def test_last_error_is_per_thread():
         results[name] = "ok"
 
     t1 = threading.Thread(target=worker, args=("a", {"causal": 0}, "non-causal"))
-    t2 = threading.Thread(target=worker, args=("b", {"window": 0}, "window must be"))
+    t2 = threading.Thread(target=worker, args=("b", {"window": -3}, "window must be"))
     t1.start(); t2.start(); t1.join(); t2.join()
     assert results == {"a": "ok", "b": "ok"}, results

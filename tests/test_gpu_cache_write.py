@@ -65,6 +65,25 @@ def test_cache_write_bit_exact(T, H, d, pages, ps, fused):
     assert np.array_equal(gv, ref_v), f"V: {np.count_nonzero(gv != ref_v)} bytes differ"
 
 
+def test_cache_write_zero_descale():
+    """An all-zero K/V tensor gets descale amax / 448 = 0: every nonzero value saturates, +-0 and
+    NaN give NaN quotients (0x7F | sign of x XOR sign of the descale); every byte as the oracle."""
+    fa = _fa()
+    T, H, d, pages, ps = 40, 2, 64, 2, 64
+    k, v, slots, kc, vc = _inputs(T, H, d, pages, ps, seed=77)
+    k[2] = 0.0
+    k[4, 0, :16] = -0.0
+    ref_k, ref_v = cache_write(k.float().numpy(), v.float().numpy(), slots.numpy(), kc.numpy(), vc.numpy(),
+                               np.float32(0.0), np.float32(0.0))
+    kcg, vcg = kc.cuda(), vc.cuda()
+    zero = torch.zeros(1, device="cuda")
+    fa.fp8attn_cache_write(k.cuda(), v.cuda(), slots.cuda(), kcg, vcg, zero, zero)
+    torch.cuda.synchronize()
+    gk, gv = kcg.cpu().numpy(), vcg.cpu().numpy()
+    assert np.array_equal(gk, ref_k), f"K: {np.count_nonzero(gk != ref_k)} bytes differ"
+    assert np.array_equal(gv, ref_v), f"V: {np.count_nonzero(gv != ref_v)} bytes differ"
+
+
 def test_cache_write_strided_views_and_null_descales():
     fa = _fa()
     T, H, d, pages, ps = 50, 4, 256, 2, 64

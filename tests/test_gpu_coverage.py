@@ -1,0 +1,204 @@
+"""GPU parity for the launch paths the workload tests reach least, through the C-ABI, against the
+fp64 CPU oracle (every row compared unless stated):
+
+* the single-P FP8 prefill instance (a q block whose first row sees at least 512 keys): the
+  sliding-window prefill at reduced size that keeps its 1024-key window, and head dims 64, 128,
+  192 and 256 with no window; each with E4M3 codes and with bf16 Q quantized in the kernel, the
+  two bit for bit equal;
+* FP8 prefill over 128-token framework blocks;
+* GQA groups that do not divide the 16-row decode tile or the 256-row prefill block (3 and 6);
+* K/V descales per (sequence, kv head) on every kernel;
+* pool slots past a sequence's length holding E4M3 NaN codes (never written for the sequence, never
+  visible): outputs bit for bit unchanged;
+* the sliding-window prefill at full size on whole q blocks, in the launch configuration the bench
+  times (bf16 Q quantized in the kernel).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from helpers import (compare, gpu_run, log, oracle_run, prefill_split_p_blocks, with_nan_tails,
+                     with_page_size)
+
+pytestmark = pytest.mark.gpu
+
+
+def _both_q_forms(w, entry, num_splits=0, label=""):
+    """E4M3 workload: the two-call path (codes checked bit for bit), then the fused call, which must
+    give the same bits; returns the outputs after checking them against the oracle."""
+    o_ref, l_ref, codes_ref = oracle_run(w)
+    o, l, codes, s = gpu_run(w, entry, num_splits=num_splits)
+    assert np.array_equal(codes, codes_ref)
+    compare(o, o_ref, l, l_ref, label=f"{label} codes S={s}")
+    o1, l1, _, s1 = gpu_run(w, entry, num_splits=num_splits, fused_q=True)
+    assert s1 == s and np.array_equal(o1, o) and np.array_equal(l1, l), f"{label}: fused Q differs"
+    return o, l
+
+
+# ------------------------------------------------------------------------------------------
+# the single-P FP8 prefill instance
+# ------------------------------------------------------------------------------------------
+SINGLE_P_CASES = {
+    # the sliding-window prefill at reduced size, keeping its window: B2 x 2048 new tokens,
+    # 4 q / 2 kv heads, d256, W1024 (most q blocks see 1024 keys)
+    "swa_prefill_window_kept": lambda: wl.custom("e4m3", 256, 4, 2, 1024, [2048, 2048], [2048, 2048], seed=41),
+    "d64_no_window": lambda: wl.custom("e4m3", 64, 4, 2, -1, [1500, 700], [1500, 300], seed=42),
+    "d128_no_window": lambda: wl.custom("e4m3", 128, 4, 2, -1, [1500, 700], [1500, 300], seed=43),
+    "d192_no_window": lambda: wl.custom("e4m3", 192, 4, 2, -1, [1500, 700], [1500, 300], seed=44),
+    "d256_no_window": lambda: wl.custom("e4m3", 256, 4, 2, -1, [1500, 700], [1500, 300], seed=45),
+    "d256_window_600_gqa8": lambda: wl.custom("e4m3", 256, 16, 2, 600, [1333, 650], [1333, 9], seed=46),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SINGLE_P_CASES))
+def test_single_p_prefill(name):
+    w = SINGLE_P_CASES[name]()
+    single, split = prefill_split_p_blocks(w)
+    log(f"[case] single-P prefill {name}: lens={w.seqlens_k_host} q={w.q_lens_host} W={w.window} "
+        f"blocks single-P={single} split-P={split}")
+    assert single > 0
+    _both_q_forms(w, "prefill", label=f"single-P {name}")
+
+
+def test_fp8_prefill_page_size_128():
+    """FP8 prefill over 128-token framework blocks (two 64-key tiles per block): the second tile of
+    a block starts at slot 64; single-P and split-P blocks both run."""
+    w = wl.custom("e4m3", 256, 4, 2, -1, [1300, 700], [1300, 300], seed=51)
+    w128 = with_page_size(w, 128)
+    single, split = prefill_split_p_blocks(w)
+    log(f"[case] FP8 prefill page 128: single-P={single} split-P={split}")
+    assert single > 0 and split > 0
+    o_ref, l_ref, _ = oracle_run(w)
+    o, l, _, _ = gpu_run(w128, "prefill")
+    compare(o, o_ref, l, l_ref, label="FP8 prefill page 128")
+    o1, l1, _, _ = gpu_run(w128, "prefill", fused_q=True)
+    assert np.array_equal(o1, o) and np.array_equal(l1, l)
+
+
+# ------------------------------------------------------------------------------------------
+# GQA groups that straddle the 16-row decode tiles and the 256-row prefill blocks
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("q_dtype,d,hq,hkv,window,seqlens,qlens,entry,splits", [
+    ("e4m3", 256, 6, 2, 300, [700, 65, 1500], [4, 16, 1], "decode", 0),
+    ("e4m3", 256, 6, 2, 300, [700, 65, 1500], [4, 16, 1], "decode", 3),
+    ("bf16", 512, 6, 2, -1, [900, 65, 1500], [7, 16, 2], "decode", 0),
+    ("bf16", 512, 6, 2, -1, [900, 65, 1500], [7, 16, 2], "decode", -5),
+    ("e4m3", 64, 12, 2, 700, [1000, 500], [13, 16], "decode", 0),
+    ("e4m3", 128, 6, 2, -1, [1100, 300], [1100, 250], "prefill", 0),
+    ("e4m3", 64, 12, 2, 700, [1000, 500], [1000, 200], "prefill", 0),
+    ("bf16", 512, 6, 2, -1, [300, 90], [300, 90], "prefill", 0),
+])
+def test_gqa_groups_not_dividing_tiles(q_dtype, d, hq, hkv, window, seqlens, qlens, entry, splits):
+    w = wl.custom(q_dtype, d, hq, hkv, window, seqlens, qlens, seed=61 + hq)
+    log(f"[case] GQA {hq // hkv} {q_dtype} d{d} W{window} L={seqlens} q={qlens} {entry} splits={splits}")
+    if q_dtype == "e4m3":
+        _both_q_forms(w, entry, num_splits=splits, label=f"GQA {hq // hkv} {entry}")
+    else:
+        o_ref, l_ref, _ = oracle_run(w)
+        o, l, _, s = gpu_run(w, entry, num_splits=splits)
+        compare(o, o_ref, l, l_ref, label=f"GQA {hq // hkv} {entry} S={s}")
+
+
+# ------------------------------------------------------------------------------------------
+# K/V descales per (sequence, kv head), on every kernel
+# ------------------------------------------------------------------------------------------
+def _per_bh_descales(w, seed):
+    """Give w K/V descales per (sequence, kv head): each (sequence, kv head) slice of the pools is
+    re-quantized with its own descale, the per-tensor one times a seeded factor in [1, 2], so the
+    dequantized values stay the workload's N(0,1) draws (up to E4M3 rounding) and the tolerance of
+    the N(0,1) recipe applies.  (Scaling the descales alone would scale the logits too.)"""
+    rng = np.random.default_rng(seed)
+    shape = (w.batch, w.num_kv_heads)
+    out = {}
+    for name, pool, ds in (("k", w.k_pool, w.k_descale), ("v", w.v_pool, w.v_descale)):
+        new_ds = (ds * torch.from_numpy(rng.uniform(1.0, 2.0, shape).astype(np.float32))).contiguous()
+        pool = pool.clone()
+        for b, L in enumerate(w.seqlens_k_host):
+            pages = w.block_table[b, :(L + 63) // 64].long()
+            for h in range(w.num_kv_heads):
+                vals = pool[pages, :, h, :].view(torch.float8_e4m3fn).float() * ds.reshape(-1)[0]
+                pool[pages, :, h, :] = (vals / new_ds[b, h]).to(torch.float8_e4m3fn).view(torch.uint8)
+        out[name] = (pool, new_ds)
+    w.k_pool, w.k_descale = out["k"]
+    w.v_pool, w.v_descale = out["v"]
+    return w
+
+
+@pytest.mark.parametrize("q_dtype,d,entry,splits,fused,window", [
+    ("e4m3", 256, "decode", 0, False, 300),
+    ("e4m3", 256, "decode", 3, True, 300),
+    ("e4m3", 128, "decode", -5, True, -1),      # balanced partition
+    ("bf16", 512, "decode", -5, False, -1),
+    ("bf16", 512, "decode", 2, False, -1),
+    ("e4m3", 256, "prefill", 0, False, -1),     # FP8 prefill, single-P and split-P blocks
+    ("e4m3", 256, "prefill", 0, True, 200),     # FP8 prefill, split-P blocks, fused Q
+    ("bf16", 128, "prefill", 0, False, -1),     # BF16 prefill
+])
+def test_per_sequence_head_descales_all_kernels(q_dtype, d, entry, splits, fused, window):
+    if entry == "decode":
+        w = wl.custom(q_dtype, d, 8, 2, window, [700, 65, 1500], [4, 16, 1], seed=71)
+    else:
+        w = wl.custom(q_dtype, d, 4, 2, window, [1200, 400, 90], [1200, 300, 90], seed=72)
+    w = _per_bh_descales(w, seed=d)
+    log(f"[case] (b,h) descales {q_dtype} d{d} {entry} splits={splits} fused={fused} W={window}")
+    o_ref, l_ref, _ = oracle_run(w)
+    o, l, _, s = gpu_run(w, entry, num_splits=splits, fused_q=fused)
+    compare(o, o_ref, l, l_ref, label=f"(b,h) descales {q_dtype} d{d} {entry} S={s}")
+
+
+# ------------------------------------------------------------------------------------------
+# slots past a sequence's length hold NaN codes: outputs unchanged bit for bit
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("q_dtype,d,hq,hkv,window,seqlens,qlens,entry,splits,fused,page", [
+    ("e4m3", 256, 8, 2, 300, [700, 65, 1501], [4, 16, 1], "decode", 0, True, 64),
+    ("e4m3", 256, 8, 2, 300, [700, 65, 1501], [4, 16, 1], "decode", 3, False, 64),
+    ("bf16", 512, 8, 2, -1, [701, 77, 1500], [1, 3, 16], "decode", -5, False, 64),
+    ("bf16", 512, 8, 2, -1, [701, 77, 1500], [1, 3, 16], "decode", 2, False, 128),
+    ("e4m3", 256, 4, 2, -1, [1333, 650], [1333, 9], "prefill", 0, True, 64),     # single-P and split-P
+    ("e4m3", 128, 4, 2, 100, [1333, 650], [1333, 9], "prefill", 0, False, 64),   # split-P only
+    ("e4m3", 256, 4, 2, -1, [1333, 650], [1333, 9], "prefill", 0, False, 128),
+    ("bf16", 128, 4, 2, -1, [333, 650], [333, 9], "prefill", 0, False, 64),
+])
+def test_nan_codes_past_sequence_end(q_dtype, d, hq, hkv, window, seqlens, qlens, entry, splits, fused, page):
+    w = wl.custom(q_dtype, d, hq, hkv, window, seqlens, qlens, seed=81)
+    if page != 64:
+        w = with_page_size(w, page)
+    wn = with_nan_tails(w)
+    assert not torch.equal(wn.v_pool, w.v_pool)
+    log(f"[case] NaN tails {q_dtype} d{d} {entry} splits={splits} fused={fused} page={page}")
+    o, l, _, s = gpu_run(w, entry, num_splits=splits, fused_q=fused)
+    o2, l2, _, s2 = gpu_run(wn, entry, num_splits=splits, fused_q=fused)
+    assert s2 == s
+    assert np.isfinite(o2).all(), "a NaN past the sequence end reached the output"
+    assert np.array_equal(o2, o) and np.array_equal(l2, l)
+
+
+# ------------------------------------------------------------------------------------------
+# the sliding-window prefill at full size, whole q blocks, as the bench launches it
+# ------------------------------------------------------------------------------------------
+def test_swa_prefill_full_size_whole_blocks():
+    """B8 x 8192 new tokens, 32/16 heads, d256, W1024, bf16 Q quantized in the kernel (the launch
+    the bench times), against the oracle on every row of the first and the last q block (256 rows =
+    128 tokens x 2 heads of the GQA group, for every kv head) of sequences 0 and 7, plus 256 random
+    tokens; and the two-call path (codes compared bit for bit over the whole Q) equals it bit for
+    bit on every output."""
+    w = wl.swa_prefill(device="cuda")
+    single, split = prefill_split_p_blocks(w)
+    log(f"[case] full-size sliding-window prefill whole blocks: single-P={single} split-P={split}")
+    o1, l1, _, _ = gpu_run(w, "prefill", fused_q=True)
+    o2, l2, codes, _ = gpu_run(w, "prefill")
+    from oracle.attention import query_values
+    _, codes_ref = query_values(w.q.cpu(), "e4m3", w.q_descale.cpu())
+    assert np.array_equal(codes, codes_ref)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2), "fused and two-call prefill differ"
+    cu = w.cu_seqlens_q.cpu().numpy()
+    toks = set()
+    for b in (0, w.batch - 1):
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        toks.update(range(t0, t0 + 128))
+        toks.update(range(t1 - 128, t1))
+    toks.update(int(x) for x in np.random.default_rng(17).choice(int(cu[-1]), 256, replace=False))
+    toks = sorted(toks)
+    o_ref, l_ref, _ = oracle_run(w, tokens=toks)
+    compare(o1, o_ref, l1, l_ref, rows=toks, label=f"full-size sliding-window prefill rows={len(toks)}")

@@ -6,7 +6,8 @@ library is missing, importing this package raises: there is no fallback path.
 
 The functions carry the C names (see include/fp8attn.h):
   fp8attn_quantize_q, fp8attn_prefill_varlen, fp8attn_decode_paged,
-  fp8attn_splitkv_combine, fp8attn_cache_write, fp8attn_last_error, fp8attn_version
+  fp8attn_decode_paged_noalloc, fp8attn_splitkv_combine, fp8attn_cache_write,
+  fp8attn_last_error, fp8attn_version
 """
 from __future__ import annotations
 
@@ -76,6 +77,8 @@ _lib.fp8attn_prefill_varlen.restype = _i32
 _lib.fp8attn_decode_paged.argtypes = [ctypes.POINTER(AttnArgs), _i32, _vp, _sz, ctypes.POINTER(_sz),
                                       ctypes.POINTER(_i32), _vp]
 _lib.fp8attn_decode_paged.restype = _i32
+_lib.fp8attn_decode_paged_noalloc.argtypes = [ctypes.POINTER(AttnArgs), _i32, ctypes.POINTER(_i32), _vp]
+_lib.fp8attn_decode_paged_noalloc.restype = _i32
 _lib.fp8attn_splitkv_combine.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _vp, _i64, _i64, _vp, _vp]
 _lib.fp8attn_splitkv_combine.restype = _i32
 _lib.fp8attn_cache_write.argtypes = [_vp, _vp, _i64, _i32, _i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _i32,
@@ -251,6 +254,23 @@ def fp8attn_decode_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens
                                    ctypes.byref(used_c), _stream(stream))
     _check("fp8attn_decode_paged", st)
     return out, lse, used_c.value
+
+
+def fp8attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, max_seqlen_q,
+                                 max_seqlen_k, q_descale=None, k_descale=None, v_descale=None, softmax_scale=0.0,
+                                 window=-1, causal=True, out=None, lse=None, want_lse=True, num_splits=0,
+                                 descale_strides=(0, 0), quantize_q=False, split_q=False, stream=None):
+    """fp8attn_decode_paged with the split-KV partials in the library's static device scratch (no
+    workspace; the call allocates nothing).  Returns (out, lse, splits_used); out and lse are
+    allocated here only if the caller passes none."""
+    out, lse = _alloc_out(q, out, lse, want_lse)
+    a = make_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seqlen_k,
+                  q_descale, k_descale, v_descale, softmax_scale, window, causal, out, lse, descale_strides,
+                  quantize_q=quantize_q, split_q=split_q)
+    used = _i32(0)
+    st = _lib.fp8attn_decode_paged_noalloc(ctypes.byref(a), num_splits, ctypes.byref(used), _stream(stream))
+    _check("fp8attn_decode_paged_noalloc", st)
+    return out, lse, used.value
 
 
 def fp8attn_splitkv_combine(partial_o, partial_lse, out=None, lse=None, stream=None):

@@ -17,6 +17,13 @@
 
 #include "params.h"
 
+// ---- the allocation-free decode: split-KV partials in a static device array ------------------
+// Every GPU the library runs on holds its own copy of `scratch` from the module's load until the
+// process ends.  In host code the name `scratch` is a host-side stand-in, not a device address:
+// each device's address comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[FP8ATTN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_err;
@@ -263,6 +270,83 @@ DecodePlan plan_decode(const fp8attn_attn_args* a, int32_t requested) {
   return pl;
 }
 
+// Checks shared by both decode entry points once the plan is known (host values only).
+fp8attn_status check_plan(const char* fn, const fp8attn_attn_args* args, const DecodePlan& pl) {
+  if (pl.balanced &&
+      (int64_t)args->num_kv_heads * args->batch * pl.row_groups + pl.grid >= (int64_t)1 << 31)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: %lld row tiles are too many for a balanced partition", fn,
+                (long long)args->num_kv_heads * args->batch * pl.row_groups);
+  if (pl.grid >= (int64_t)1 << 31)
+    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: grid of %lld blocks is too large", fn, (long long)pl.grid);
+  return FP8ATTN_OK;
+}
+
+// Launches of a decode plan: the partial kernel, then the combine when the plan leaves partials.
+// workspace holds at least pl.ws_bytes (256-byte aligned) whenever pl.ws_bytes > 0.
+fp8attn_status run_decode(const char* fn, const fp8attn_attn_args* args, const DecodePlan& pl, void* workspace,
+                          hipStream_t stream) {
+  fp8attn::AttnParams p = make_params(args);
+  p.num_splits = pl.splits;
+  p.units_per_split = pl.units_per_split;
+  p.row_groups = pl.row_groups;
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (pl.balanced) {
+    const size_t items = (size_t)args->num_kv_heads * args->batch * pl.row_groups;
+    const size_t slots = (size_t)pl.grid + items;
+    p.part_o = reinterpret_cast<float*>(ws);
+    p.part_lse = reinterpret_cast<float*>(ws + round_up(slots * 16 * args->head_dim * sizeof(float)));
+    p.seg_meta = reinterpret_cast<int32_t*>(ws + round_up(slots * 16 * args->head_dim * sizeof(float)) +
+                                            round_up(slots * 16 * sizeof(float)));
+  } else if (pl.splits > 1) {
+    const size_t rows = (size_t)args->total_q * args->num_q_heads;
+    p.part_o = reinterpret_cast<float*>(ws);
+    p.part_lse = reinterpret_cast<float*>(ws + round_up((size_t)pl.splits * rows * args->head_dim * sizeof(float)));
+  }
+  hipError_t e = fp8attn::launch_decode(p, args->q_dtype, args->head_dim, pl.grid, stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  if (pl.balanced) {
+    e = fp8attn::launch_combine_parts(p.part_o, p.part_lse, p.seg_meta, args->cu_seqlens_q, args->batch,
+                                      pl.row_groups, args->num_kv_heads, args->num_q_heads / args->num_kv_heads,
+                                      (int32_t)pl.grid, args->head_dim, args->out, args->out_stride_tok, args->out_stride_head,
+                                      args->lse, stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  } else if (pl.splits > 1) {
+    e = fp8attn::launch_combine(p.part_o, p.part_lse, pl.splits, args->total_q, args->num_q_heads, args->head_dim,
+                                args->out, args->out_stride_tok, args->out_stride_head, args->lse, stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
+  return ok();
+}
+
+fp8attn_status scratch_address(const char* fn, void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  if (dev < 0 || dev >= 64) return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: device index %d: at most 64 devices", fn, dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (!a || !aligned(a, kAlign))
+      return fail(FP8ATTN_ERR_HIP, "%s: the scratch array of device %d is not %zu-byte aligned", fn, dev, kAlign);
+    addr[dev] = a;
+  }
+  *out = addr[dev];
+  return FP8ATTN_OK;
+}
+
+fp8attn_status decode_checks(const char* fn, const fp8attn_attn_args* args, int32_t num_splits) {
+  fp8attn_status st = validate_attn(fn, args, true);
+  if (st != FP8ATTN_OK) return st;
+  if (num_splits < -kMaxParts)
+    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: num_splits %d: a balanced partition takes at most %d parts", fn,
+                num_splits, kMaxParts);
+  return FP8ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -353,11 +437,8 @@ fp8attn_status fp8attn_decode_paged(const fp8attn_attn_args* args, int32_t num_s
                                     size_t workspace_bytes, size_t* workspace_needed, int32_t* num_splits_used,
                                     hipStream_t stream) {
   const char* fn = "fp8attn_decode_paged";
-  fp8attn_status st = validate_attn(fn, args, true);
+  fp8attn_status st = decode_checks(fn, args, num_splits);
   if (st != FP8ATTN_OK) return st;
-  if (num_splits < -kMaxParts)
-    return fail(FP8ATTN_ERR_INVALID_ARG, "%s: num_splits %d: a balanced partition takes at most %d parts", fn,
-                num_splits, kMaxParts);
   if (args->total_q == 0 || args->batch == 0) {
     if (workspace_needed) *workspace_needed = 0;
     if (num_splits_used) *num_splits_used = 1;
@@ -367,16 +448,8 @@ fp8attn_status fp8attn_decode_paged(const fp8attn_attn_args* args, int32_t num_s
   if (workspace_needed) *workspace_needed = pl.ws_bytes;
   if (num_splits_used) *num_splits_used = pl.splits;
   if (!workspace && workspace_needed) return ok();  // size query
-  if (pl.balanced &&
-      (int64_t)args->num_kv_heads * args->batch * pl.row_groups + pl.grid >= (int64_t)1 << 31)
-    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: %lld row tiles are too many for a balanced partition", fn,
-                (long long)args->num_kv_heads * args->batch * pl.row_groups);
-  if (pl.grid >= (int64_t)1 << 31)
-    return fail(FP8ATTN_ERR_UNSUPPORTED, "%s: grid of %lld blocks is too large", fn, (long long)pl.grid);
-  fp8attn::AttnParams p = make_params(args);
-  p.num_splits = pl.splits;
-  p.units_per_split = pl.units_per_split;
-  p.row_groups = pl.row_groups;
+  st = check_plan(fn, args, pl);
+  if (st != FP8ATTN_OK) return st;
   if (pl.ws_bytes > 0) {
     if (!workspace || workspace_bytes < pl.ws_bytes)
       return fail(FP8ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed for %s %d, got %zu", fn,
@@ -385,33 +458,33 @@ fp8attn_status fp8attn_decode_paged(const fp8attn_attn_args* args, int32_t num_s
     if (!aligned(workspace, kAlign))
       return fail(FP8ATTN_ERR_INVALID_ARG, "%s: workspace must be %zu-byte aligned", fn, kAlign);
   }
-  char* ws = reinterpret_cast<char*>(workspace);
-  if (pl.balanced) {
-    const size_t items = (size_t)args->num_kv_heads * args->batch * pl.row_groups;
-    const size_t slots = (size_t)pl.grid + items;
-    p.part_o = reinterpret_cast<float*>(ws);
-    p.part_lse = reinterpret_cast<float*>(ws + round_up(slots * 16 * args->head_dim * sizeof(float)));
-    p.seg_meta = reinterpret_cast<int32_t*>(ws + round_up(slots * 16 * args->head_dim * sizeof(float)) +
-                                            round_up(slots * 16 * sizeof(float)));
-  } else if (pl.splits > 1) {
-    const size_t rows = (size_t)args->total_q * args->num_q_heads;
-    p.part_o = reinterpret_cast<float*>(ws);
-    p.part_lse = reinterpret_cast<float*>(ws + round_up((size_t)pl.splits * rows * args->head_dim * sizeof(float)));
+  return run_decode(fn, args, pl, workspace, stream);
+}
+
+fp8attn_status fp8attn_decode_paged_noalloc(const fp8attn_attn_args* args, int32_t num_splits,
+                                            int32_t* num_splits_used, hipStream_t stream) {
+  const char* fn = "fp8attn_decode_paged_noalloc";
+  fp8attn_status st = decode_checks(fn, args, num_splits);
+  if (st != FP8ATTN_OK) return st;
+  if (args->total_q == 0 || args->batch == 0) {
+    if (num_splits_used) *num_splits_used = 1;
+    return ok();
   }
-  hipError_t e = fp8attn::launch_decode(p, args->q_dtype, args->head_dim, pl.grid, stream);
-  if (e != hipSuccess) return hip_fail(fn, e);
-  if (pl.balanced) {
-    e = fp8attn::launch_combine_parts(p.part_o, p.part_lse, p.seg_meta, args->cu_seqlens_q, args->batch,
-                                      pl.row_groups, args->num_kv_heads, args->num_q_heads / args->num_kv_heads,
-                                      (int32_t)pl.grid, args->head_dim, args->out, args->out_stride_tok, args->out_stride_head,
-                                      args->lse, stream);
-    if (e != hipSuccess) return hip_fail(fn, e);
-  } else if (pl.splits > 1) {
-    e = fp8attn::launch_combine(p.part_o, p.part_lse, pl.splits, args->total_q, args->num_q_heads, args->head_dim,
-                                args->out, args->out_stride_tok, args->out_stride_head, args->lse, stream);
-    if (e != hipSuccess) return hip_fail(fn, e);
+  const DecodePlan pl = plan_decode(args, num_splits);
+  if (num_splits_used) *num_splits_used = pl.splits;
+  st = check_plan(fn, args, pl);
+  if (st != FP8ATTN_OK) return st;
+  if (pl.ws_bytes > FP8ATTN_NOALLOC_SCRATCH_BYTES)
+    return fail(FP8ATTN_ERR_WORKSPACE, "%s: %s %d needs %zu bytes of split-KV scratch, more than the %zu of the "
+                "static scratch array; call fp8attn_decode_paged with a workspace (or ask for fewer splits)", fn,
+                pl.balanced ? "a balanced partition of parts" : "split count", pl.balanced ? -pl.splits : pl.splits,
+                pl.ws_bytes, (size_t)FP8ATTN_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (pl.ws_bytes > 0) {
+    st = scratch_address(fn, &ws);
+    if (st != FP8ATTN_OK) return st;
   }
-  return ok();
+  return run_decode(fn, args, pl, ws, stream);
 }
 
 fp8attn_status fp8attn_prefill_varlen(const fp8attn_attn_args* args, hipStream_t stream) {

@@ -173,6 +173,24 @@ fp8attn_status fp8attn_decode_paged(const fp8attn_attn_args* args, int32_t num_s
                                     hipStream_t stream);
 
 /*
+ * fp8attn_decode_paged without a workspace, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same validation,
+ * plan, kernels and results as fp8attn_decode_paged with the same num_splits (bit for bit); the
+ * split-KV partials live in a static device array of FP8ATTN_NOALLOC_SCRATCH_BYTES (32 MiB) that
+ * every GPU the library runs on holds from the library's load until the process ends.  The call
+ * allocates nothing.  Its first call on a device looks up that device's array address once.
+ *   num_splits, num_splits_used: as for fp8attn_decode_paged
+ * A plan that needs more partials than the array holds returns FP8ATTN_ERR_WORKSPACE before any
+ * launch (fp8attn_decode_paged with a workspace takes any size).  Every call on one GPU shares
+ * that GPU's array and it keeps the last call's contents: calls that overlap on one GPU (several
+ * streams or threads) race on it, so the caller serializes them.  Nothing needs clearing between
+ * calls: every partial a call reads, the same call wrote.
+ */
+#define FP8ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+fp8attn_status fp8attn_decode_paged_noalloc(const fp8attn_attn_args* args, int32_t num_splits,
+                                            int32_t* num_splits_used, hipStream_t stream);
+
+/*
  * Log-sum-exp merge of split-KV partials ([60372] Details: the combine work of split-KV).
  * For each row n (a (token, q head) pair) and split s:
  *   M = max_s lse[s,n];  w_s = exp(lse[s,n] - M)  (a split with lse = -inf has weight 0 and its

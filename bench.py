@@ -9,9 +9,11 @@ bytes of the visible keys and values plus Q read and O written, divided by the s
 Four independently drawn input sets rotate so that the working set exceeds the 256 MiB MALL.
 
 ``roofline`` covers the attention kernel alone, timed with HIP events on the stream it runs on.
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.  ``extra``
-reports the other workload shapes (full-attention decode, spec-verify with a shared prefix,
-sliding-window prefill) with their own roofline fractions.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload (and, with one BLAS
+thread, on one pass and on the tiny workload).  ``extra`` reports the other workload shapes
+(full-attention decode, spec-verify with a shared prefix, sliding-window prefill, d512 prefill),
+each with its own ``roofline`` object (HBM GB/s or MFMA TFLOP/s against the MI355X peak), and the
+spec-verify lines with the cache-aware bound (each distinct page read once, or its MFMA work).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--profile-pass]
 """
@@ -89,6 +91,18 @@ def algo_bytes(w, fused=True):
     qb = w.total_q * w.num_q_heads * w.head_dim * (1 if (w.q_dtype == "e4m3" and not fused) else 2)
     ob = w.total_q * w.num_q_heads * w.head_dim * 2
     return kv + qb + ob, kv
+
+
+def unique_kv_bytes(w):
+    """Bytes of the distinct pages that hold visible keys, K and V (shared-prefix pages once): what a
+    kernel that kept every shared page on chip after its first read would fetch from HBM."""
+    ps = w.k_pool.shape[1]
+    bt = w.block_table.cpu().numpy()
+    pages = set()
+    for b, (L, ql) in enumerate(zip(w.seqlens_k_host, w.q_lens_host)):
+        lo = 0 if w.window < 1 else max(0, L - ql - w.window + 1)
+        pages.update(int(x) for x in bt[b, lo // ps:(L - 1) // ps + 1])
+    return len(pages) * ps * w.num_kv_heads * w.head_dim * 2
 
 
 def algo_flops(w):
@@ -332,7 +346,6 @@ def cpu_baseline(budget_s=15.0):
     bt = full.block_table.cpu().numpy()
     cu = full.cu_seqlens_q.cpu().numpy()
     sk = full.seqlens_k.cpu().numpy()
-    done_bytes, nseq, t_used, passes = 0, 0, 0.0, 0
     hosts = []
     for b in range(full.batch):
         L = int(sk[b])
@@ -344,22 +357,45 @@ def cpu_baseline(budget_s=15.0):
         k[pages] = full.k_pool.index_select(0, ids).cpu().numpy()
         v[pages] = full.v_pool.index_select(0, ids).cpu().numpy()
         hosts.append((k, v, (L - lo) * full.num_kv_heads * 256 * 2 + 32 * 256 * 1 + 32 * 256 * 2))
-    while t_used < budget_s:          # whole passes over the batch until the budget is spent
-        for b in range(full.batch):
-            k, v, nbytes = hosts[b]
+    def run(budget):
+        done, used, npass = 0, 0.0, 0
+        while npass == 0 or used < budget:    # whole passes over the batch until the budget is spent
+            for b in range(full.batch):
+                k, v, nbytes = hosts[b]
+                t0 = time.perf_counter()
+                paged_attention(qv[cu[b]:cu[b + 1]], k, v, bt[b:b + 1], np.array([0, 1]), sk[b:b + 1],
+                                full.num_kv_heads, default_scale(256), full.window, full.k_descale.cpu(),
+                                full.v_descale.cpu())
+                used += time.perf_counter() - t0
+                done += nbytes
+            npass += 1
+        return done, used, npass
+
+    done_bytes, t_used, passes = run(budget_s)
+    # the same oracle with its BLAS held to one thread, on one pass over the batch, and on the tiny
+    # workload (1 sequence, 1/1 heads, d64, 128 keys, 16 queries)
+    with threadpoolctl.threadpool_limits(1):
+        d1, t1, p1 = run(0.0)
+        tiny = wl.tiny("e4m3")
+        tq, _ = query_values(tiny.q, "e4m3", tiny.q_descale)
+        tb = tiny.seqlens_k_host[0] * 64 * 2 + 16 * 64 * 3
+        reps, t_tiny = 0, 0.0
+        while reps == 0 or t_tiny < 1.0:
             t0 = time.perf_counter()
-            paged_attention(qv[cu[b]:cu[b + 1]], k, v, bt[b:b + 1], np.array([0, 1]), sk[b:b + 1],
-                            full.num_kv_heads, default_scale(256), full.window, full.k_descale.cpu(),
-                            full.v_descale.cpu())
-            t_used += time.perf_counter() - t0
-            done_bytes += nbytes
-            nseq += 1
-        passes += 1
+            paged_attention(tq, tiny.k_pool, tiny.v_pool, tiny.block_table, tiny.cu_seqlens_q, tiny.seqlens_k, 1,
+                            default_scale(64), -1, tiny.k_descale, tiny.v_descale)
+            t_tiny += time.perf_counter() - t0
+            reps += 1
     del full
     torch.cuda.empty_cache()
     return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"the whole sliding-window decode workload (32 sequences, all 32 q heads, 1024 "
-                      f"visible keys each), {passes} passes, numpy fp64, {t_used:.1f} s"}
+                      f"visible keys each), {passes} passes, numpy fp64, {t_used:.1f} s",
+            "one_thread": {"sliding_window_decode": {"value": d1 / t1 / 1e9, "unit": "GB/s", "seconds": round(t1, 2),
+                                                     "sample": f"{p1} pass over the 32 sequences"},
+                           "tiny": {"value": tb / (t_tiny / reps) / 1e9, "unit": "GB/s",
+                                    "ms_per_call": round(t_tiny / reps * 1e3, 3),
+                                    "sample": f"{reps} calls on the tiny d64 workload (128 keys, 16 queries)"}}}
 
 
 def load_traffic(kernel_key):
@@ -473,11 +509,24 @@ def main():
                     "swa_prefill": ["prefill_swa", "prefill_swa_splitp"]}.get(name)
             tr = [load_traffic(k) for k in keys] if keys else [None]
             e["traffic"] = sum(tr) if fz and all(t is not None for t in tr) else None
+            mfma_peak = FP8_PEAK_TFLOPS if ww.q_dtype == "e4m3" or split else BF16_PEAK_TFLOPS
             if bound == "hbm":
                 e["hbm_frac"] = round(e["kv_read_GBps"] / HBM_PEAK_GBS, 4)
+                e["roofline"] = {"bound": "hbm", "achieved": e["kv_read_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": e["hbm_frac"], "traffic": e["traffic"], "algorithmic_bytes_per_launch": tb}
             else:
-                peak = FP8_PEAK_TFLOPS if ww.q_dtype == "e4m3" or split else BF16_PEAK_TFLOPS
-                e["mfma_frac"] = round(e["TFLOPs"] / peak, 4)
+                e["mfma_frac"] = round(e["TFLOPs"] / mfma_peak, 4)
+                e["roofline"] = {"bound": "mfma", "achieved": e["TFLOPs"], "peak": mfma_peak, "unit": "TFLOP/s",
+                                 "frac": e["mfma_frac"], "traffic": e["traffic"], "algorithmic_flops_per_launch": fl}
+            if name.startswith("spec_verify"):
+                # the shared prefix need not come from HBM once per sequence: the bound of a kernel that
+                # reads each distinct page once, or of its MFMA work, whichever is longer
+                ub = unique_kv_bytes(ww)
+                hbm_ms = ub / (HBM_PEAK_GBS * 1e9) * 1e3
+                mfma_ms = fl / (mfma_peak * 1e12) * 1e3
+                e["cache_aware"] = {"unique_kv_bytes": ub, "hbm_bound_ms": round(hbm_ms, 4),
+                                    "mfma_bound_ms": round(mfma_ms, 4), "bound_ms": round(max(hbm_ms, mfma_ms), 4),
+                                    "frac": round(max(hbm_ms, mfma_ms) / r["kernel_ms"], 4)}
             extra[name] = e
         for name, make, ns in [("swa_decode_graph", lambda s: wl.swa_decode(device="cuda", seed=100 + s), nsets),
                                ("full_decode_graph", lambda s: wl.full_decode(device="cuda", seed=200 + s), 4)]:

@@ -85,3 +85,27 @@ def test_full_attention_bytes_scale_with_lengths():
     w = _shape(seqlens, [1, 1, 1], -1, 32, 4, 512, q_dtype="bf16")
     _, kv = bench.algo_bytes(w)
     assert kv == sum(seqlens) * 4 * 512 * 2
+
+
+def test_unique_kv_bytes_spec_verify_closed_form():
+    """The cache-aware bound of the spec-verify workload reads each distinct page once: 400 prefix
+    pages shared by all 64 sequences plus 48 unique pages each = 3,472 pages of 64 tokens x 4 kv
+    heads x 512 bytes, K and V: 910,163,968 bytes."""
+    import torch
+    B, prefix, own = 64, 400, 48
+    table = np.zeros((B, prefix + own), dtype=np.int64)
+    nxt = prefix
+    for b in range(B):
+        table[b, :prefix] = np.arange(prefix)
+        table[b, prefix:] = np.arange(nxt, nxt + own)
+        nxt += own
+    w = _shape([(prefix + own) * 64] * B, [4] * B, -1, 32, 4, 512, "bf16")
+    w.k_pool = SimpleNamespace(shape=(nxt, 64, 4, 512))
+    w.block_table = torch.from_numpy(table)
+    assert bench.unique_kv_bytes(w) == 3472 * 64 * 4 * 512 * 2 == 910_163_968
+    # with a window, only the pages of the visible keys count
+    w2 = _shape([1000], [1], 100, 2, 1, 64)
+    w2.k_pool = SimpleNamespace(shape=(16, 64, 1, 64))
+    w2.block_table = torch.arange(16).reshape(1, 16)
+    # keys 900..999 sit in pages 14 and 15
+    assert bench.unique_kv_bytes(w2) == 2 * 64 * 64 * 2

@@ -423,7 +423,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="only the main workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--profile-pass", default=None,
-                    choices=["swa_decode", "full_decode", "spec_verify", "swa_prefill", "kv_write_swa_prefill"],
+                    choices=["swa_decode", "full_decode", "spec_verify", "swa_prefill", "full_prefill",
+                             "kv_write_swa_prefill"],
                     help="short run for rocprofv3 counter passes: one workload plus a 1 GiB device copy")
     ap.add_argument("--separate-quantize", action="store_true",
                     help="quantize Q with its own call before attention (two launches per step) instead of "
@@ -447,6 +448,7 @@ def main():
         "full_decode": (lambda s: wl.full_decode(device="cuda", seed=200 + s), "decode"),
         "spec_verify": (lambda s: wl.spec_verify(device="cuda", seed=300 + s), "decode"),
         "swa_prefill": (lambda s: wl.swa_prefill(device="cuda", seed=400 + s), "prefill"),
+        "full_prefill": (lambda s: wl.full_prefill(device="cuda", seed=500 + s), "prefill"),
     }
     if args.profile_pass:
         # a plain copy of known size (1 GiB read + 1 GiB written) calibrates FETCH_SIZE / WRITE_SIZE

@@ -195,11 +195,13 @@ fp8attn::AttnParams make_params(const fp8attn_attn_args* a) {
   p.lse = a->lse;
   p.max_seqlen_q = a->max_seqlen_q;
   p.num_splits = 1;
+  p.tile_rows = 16;
   return p;
 }
 
 struct DecodePlan {
   int32_t row_groups;
+  int32_t tile_rows;         // 16, or 32 (split grid with more than 16 rows per sequence and kv head)
   int32_t max_units;
   int32_t splits;            // split count, or minus the partition count (balanced partition)
   int32_t units_per_split;
@@ -214,7 +216,11 @@ struct DecodePlan {
 // equal lengths), and more splits cost more than they balance (1.14 ms at 16).  Short ranges
 // (a 1024-key window) are uniform by construction and keep the one-kernel plan; several row
 // tiles per sequence (spec-decode verify) keep theirs, because the split grid runs a
-// sequence's tiles side by side and they share its K/V in L2.
+// sequence's tiles side by side.
+// The split grid takes 32-row tiles when a sequence has more than 16 rows per kv head and the head
+// dim is at most 256: each K/V unit is then loaded once for 32 rows instead of once per 16.  At
+// head dim 512 the two halves' O accumulators alone fill the 256 accumulation registers of a wave
+// and the kernel spilled in its loop (5x slower), so 512 keeps 16-row tiles.
 constexpr int32_t kBalancedMinUnits = 256;   // 4096 keys
 constexpr int32_t kMaxParts = 1 << 20;
 
@@ -231,11 +237,13 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 DecodePlan plan_decode(const fp8attn_attn_args* a, int32_t requested) {
   DecodePlan pl{};
   const int G = a->num_q_heads / a->num_kv_heads;
-  pl.row_groups = (a->max_seqlen_q * G + 15) / 16;
+  const int64_t rows = (int64_t)a->max_seqlen_q * G;
+  pl.tile_rows = 16;
+  pl.row_groups = (int32_t)((rows + 15) / 16);
   int64_t vis = a->max_seqlen_k;
   if (a->window >= 1) vis = std::min<int64_t>(vis, (int64_t)a->window + a->max_seqlen_q - 1);
   pl.max_units = (int32_t)((vis + 15) / 16 + 1);
-  const int64_t items = (int64_t)a->num_kv_heads * a->batch * pl.row_groups;
+  int64_t items = (int64_t)a->num_kv_heads * a->batch * pl.row_groups;
   const int64_t per_cu = a->head_dim > 256 ? 1 : a->head_dim > 64 ? 2 : 4;
   if (requested < 0 || (requested == 0 && pl.row_groups == 1 && pl.max_units >= kBalancedMinUnits)) {
     // balanced partition into R parts: one block per part, all resident at once in automatic mode
@@ -248,6 +256,11 @@ DecodePlan plan_decode(const fp8attn_attn_args* a, int32_t requested) {
                   round_up((size_t)items * 2 * sizeof(int32_t));
     pl.grid = R;
     return pl;
+  }
+  if (rows > 16 && a->head_dim <= 256) {
+    pl.tile_rows = 32;
+    pl.row_groups = (int32_t)((rows + 31) / 32);
+    items = (int64_t)a->num_kv_heads * a->batch * pl.row_groups;
   }
   int64_t S;
   if (requested > 0) {
@@ -289,6 +302,7 @@ fp8attn_status run_decode(const char* fn, const fp8attn_attn_args* args, const D
   p.num_splits = pl.splits;
   p.units_per_split = pl.units_per_split;
   p.row_groups = pl.row_groups;
+  p.tile_rows = pl.tile_rows;
   char* ws = reinterpret_cast<char*>(workspace);
   if (pl.balanced) {
     const size_t items = (size_t)args->num_kv_heads * args->batch * pl.row_groups;
@@ -498,9 +512,12 @@ fp8attn_status fp8attn_prefill_varlen(const fp8attn_attn_args* args, hipStream_t
     e = fp8attn::launch_prefill_fp8(p, args->head_dim, args->q_dtype == FP8ATTN_BF16_TO_E4M3, stream);
   } else {
     // BF16 queries, and head dim 96 (whose rows do not split into the prefill tiles' 64-byte
-    // k-steps): the split-KV kernel over 16-row query tiles, one split per tile.
+    // k-steps): the split-KV kernel over 32-row query tiles (16 when no sequence has more rows
+    // per kv head), one split per tile.
     const int G = args->num_q_heads / args->num_kv_heads;
-    p.row_groups = (args->max_seqlen_q * G + 15) / 16;
+    const int64_t rows = (int64_t)args->max_seqlen_q * G;
+    p.tile_rows = rows > 16 && args->head_dim <= 256 ? 32 : 16;
+    p.row_groups = (int32_t)((rows + p.tile_rows - 1) / p.tile_rows);
     p.num_splits = 1;
     p.units_per_split = (int32_t)(((int64_t)args->max_seqlen_k + 15) / 16 + 1);
     const int64_t grid = (int64_t)args->num_kv_heads * args->batch * p.row_groups;

@@ -606,6 +606,442 @@ __global__ void __launch_bounds__(256)
   decode_tile<QM, D, false>(p, b, h, rt, o0, o0 + p.units_per_split, s, p.num_splits == 1);
 }
 
+// ---- 32-row tiles ------------------------------------------------------------------------------
+// A tile of 32 rows, two 16-row halves (the MFMA's column count), for decode steps with more than
+// 16 rows per (sequence, kv head) such as speculative-decode verification (GQA 8 x 4 query tokens):
+// every K/V unit is loaded, and for BF16 Q dequantized, once for both halves instead of once per
+// 16-row tile, which halves the K/V stream of such steps.  The four waves split the key range as in
+// decode_tile, with the same mask, softmax, PV and merge.  Q lives in LDS as the image of the MFMA
+// B operands, written once by waves 0 and 1 before the loop; the registers it frees hold the second
+// half's O accumulators.  Head dims up to 256 (at 512 the two halves' accumulators alone take a
+// wave's 256 accumulation registers).
+template <int QM, int D>
+__device__ __forceinline__ void decode_tile32(const AttnParams& p, const int b, const int h, const int rt,
+                                              const int o0, const int o1, const int pidx, const bool whole) {
+  constexpr bool QFP8 = QM != kQBf16;   // QK^T on the FP8 MFMA
+  constexpr bool SPLIT = QM == kQBf16Split;
+  constexpr int DP = D == 96 ? 128 : D;
+  using S = DecodeShape<DP>;
+  using T = DecodeTune<QFP8, DP>;
+  constexpr int NBUF = T::NBUF;
+  constexpr int NQ = 2 * S::KCH;                      // B operands per half (16 d values each)
+  constexpr int QB = QFP8 ? 8 : 16;                   // bytes of one lane's operand
+  constexpr int QIMG = 2 * NQ * 64 * QB;              // image [half][operand][lane] (split Q: hi)
+  constexpr int QLDS = SPLIT ? 2 * QIMG : QIMG;       // (split Q: the lo image follows)
+  constexpr int MERGE = 4 * 16 * S::RS * 4;           // one half's O of the 4 waves, fp32
+  __shared__ __attribute__((aligned(16))) uint8_t smem[QLDS > MERGE ? QLDS : MERGE];
+  __shared__ float sm_m[4][16];
+  __shared__ float sm_l[4][16];
+  __shared__ float sm_cs[32];
+  float (*sm_o)[16][S::RS] = reinterpret_cast<float (*)[16][S::RS]>(smem);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int G = p.group;
+
+  // per-item scalars, requested together (see decode_tile)
+  const int64_t dsi = (int64_t)b * p.ds_stride_b + (int64_t)h * p.ds_stride_h;
+  const int t0 = load_uniform(p.cu_seqlens_q, b);
+  const int t1 = load_uniform(p.cu_seqlens_q, b + 1);
+  const int L = load_uniform(p.seqlens_k, b);
+  const float* stand_in = reinterpret_cast<const float*>(p.seqlens_k);
+  const float kd_raw = load_uniform(p.k_descale ? p.k_descale : stand_in, p.k_descale ? dsi : 0);
+  const float vd_raw = load_uniform(p.v_descale ? p.v_descale : stand_in, p.v_descale ? dsi : 0);
+  const float qd_raw = load_uniform(p.q_descale ? p.q_descale : stand_in, 0);
+  asm volatile("" ::"s"(t0), "s"(t1), "s"(L), "s"(kd_raw), "s"(vd_raw), "s"(qd_raw));
+  const int ql = t1 - t0;
+  const int nrows = ql * G;
+  const int row0 = rt * 32;
+  if (row0 >= nrows) return;
+  const int rlast = min(row0 + 32, nrows) - 1;
+  const int p_first = L - ql + row0 / G;
+  const int p_last = L - ql + rlast / G;
+  const int W = p.window;
+  const int k_lo = W >= 1 ? max(0, p_first - W + 1) : 0;
+  const int u_begin = k_lo / 16;
+  const int u_end = (p_last + 16) / 16;
+  const int su0 = u_begin + o0;
+  const int su1 = min(u_end, u_begin + o1);
+  const int full_lo = W >= 1 ? p_last - W + 1 : 0;   // keys [full_lo, p_first] are seen by every row
+
+  // this lane's row in each half
+  int tok[2], hqr[2], pos[2];
+  bool rvalid[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int r = row0 + 16 * hh + col;
+    rvalid[hh] = r < nrows;
+    tok[hh] = (rvalid[hh] ? r : rlast) / G;
+    hqr[hh] = h * G + (rvalid[hh] ? r : rlast) % G;
+    pos[hh] = L - ql + tok[hh];
+  }
+
+  if (su0 >= su1) {  // nothing visible in this split: neutral partial for the combine
+    if (!whole && threadIdx.x < 32) {
+      const int r = row0 + (int)threadIdx.x;
+      if (r < nrows) p.part_lse[((int64_t)pidx * p.total_q + t0 + r / G) * p.hq + h * G + r % G] = kNegInf;
+    }
+    return;
+  }
+
+  const float kd = p.k_descale ? kd_raw : 1.0f;
+  const float vd = p.v_descale ? vd_raw : 1.0f;
+  const float qd = QFP8 && p.q_descale ? qd_raw : 1.0f;
+  const float cscale = p.scale_log2 * kd * qd;
+
+  // page ids of the split's keys, one per lane (see decode_tile)
+  const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
+  const int ps = p.page_size;
+  const int pg_last = ((su1 - 1) * 16) / ps;
+  int pg_base = (su0 * 16) / ps;
+  int pg_vec = bt[min(pg_base + lane, pg_last)];
+
+  const uint8_t* kbase = p.k_cache + (int64_t)h * p.kv_stride_head;
+  const uint8_t* vbase = p.v_cache + (int64_t)h * p.kv_stride_head;
+  const int64_t sT = p.kv_stride_tok, sP = p.kv_stride_page;
+  auto page_of = [&](int u) __attribute__((always_inline)) -> int {
+    const int pi = (u * 16) / ps;
+    if (pi - pg_base >= 64) {
+      pg_base = pi;
+      pg_vec = bt[min(pi + lane, pg_last)];
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    return __builtin_amdgcn_readlane(pg_vec, pi - pg_base);
+  };
+  const bool k_hi_ok = 64 * (S::KCH - 1) + 16 * grp < D;
+  const bool v_ok = col * S::CW < D;
+  UnitOffsets uoff;
+  uoff.k = (uint32_t)(col * sT) + 16u * (uint32_t)grp;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) uoff.v[i] = (uint32_t)((4 * grp + i) * sT) + (uint32_t)(col * S::CW);
+  const int ulast = su1 - 1;
+  auto issue = [&](UnitRegs<DP>& ur, int u) __attribute__((always_inline)) {
+    const bool trailing = u > ulast;
+    const int uc = trailing ? ulast : u;
+    const int64_t unit = page_of(uc) * sP + (int64_t)((uc * 16) % ps) * sT;
+    const uint32_t nrec = (uint32_t)min(16, L - uc * 16) * (uint32_t)sT;
+    UnitOffsets o = uoff;
+    o.k = trailing ? 0u : o.k;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.v[i] = trailing ? 0u : o.v[i];
+    load_unit<DP, D, T::NT>(ur, unit_rsrc(kbase + unit, nrec), unit_rsrc(vbase + unit, nrec), o, k_hi_ok, v_ok);
+  };
+
+  // the first units' loads go out before Q is staged, so their latencies overlap
+  const int u0 = su0 + wave;
+  UnitRegs<DP> buf[NBUF];
+#pragma unroll
+  for (int k = 0; k < NBUF; ++k) issue(buf[k], u0 + 4 * k);
+
+  // ---- Q: wave hh (0 or 1) writes the B-operand image of half hh ------------------------------
+  // Operand i of half hh, lane l: row 16 hh + l % 16, d values 64 (i / 2) + 16 (l / 16) + 8 (i % 2)
+  // .. + 7 (the layout of decode_tile's Q registers), at byte ((hh NQ + i) 64 + l) QB.
+  if (wave < 2) {
+    const int hh = wave;
+    const int64_t qrow = (int64_t)(t0 + tok[hh]) * p.q_stride_tok + (int64_t)hqr[hh] * p.q_stride_head + 16 * grp;
+    uint8_t* img = smem + (size_t)(hh * NQ * 64 + lane) * QB;
+    if constexpr (QM == kQE4M3) {
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) + qrow;
+#pragma unroll
+      for (int c = 0; c < S::KCH; ++c) {
+        const bool ok = rvalid[hh] && (D == DP || 64 * c + 16 * grp < D);
+        const u32x4_t w = ok ? *reinterpret_cast<const u32x4_t*>(qp + 64 * c) : u32x4_t{0, 0, 0, 0};
+        *reinterpret_cast<uint64_t*>(img + (2 * c) * 64 * QB) = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
+        *reinterpret_cast<uint64_t*>(img + (2 * c + 1) * 64 * QB) = (uint64_t)w[2] | ((uint64_t)w[3] << 32);
+      }
+    } else if constexpr (QM == kQBf16) {
+      const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + qrow;
+#pragma unroll
+      for (int c = 0; c < S::KCH; ++c) {
+        const bool ok = rvalid[hh] && (D == DP || 64 * c + 16 * grp < D);
+        const bf16x8_t z = {};
+        *reinterpret_cast<bf16x8_t*>(img + (2 * c) * 64 * QB) = ok ? *reinterpret_cast<const bf16x8_t*>(qp + 64 * c) : z;
+        *reinterpret_cast<bf16x8_t*>(img + (2 * c + 1) * 64 * QB) =
+            ok ? *reinterpret_cast<const bf16x8_t*>(qp + 64 * c + 8) : z;
+      }
+    } else {
+      // bf16 Q, quantized (BF16_TO_E4M3) or split into two E4M3 terms (split Q); a row past the
+      // end reads the clamped row
+      const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + qrow;
+      u32x4_t qraw[NQ];
+#pragma unroll
+      for (int c = 0; c < S::KCH; ++c) {
+        const bool ok = D == DP || 64 * c + 16 * grp < D;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          qraw[2 * c + hf] = ok ? *reinterpret_cast<const u32x4_t*>(qp + 64 * c + 8 * hf) : u32x4_t{0, 0, 0, 0};
+      }
+      if constexpr (QM == kQBf16E4M3) {
+        const double rcp = 1.0 / (double)qd;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+          const u32x2_t e = quantize8_bf16_e4m3(qraw[i], rcp);
+          *reinterpret_cast<uint64_t*>(img + i * 64 * QB) = rvalid[hh] ? ((uint64_t)e[0] | ((uint64_t)e[1] << 32)) : 0;
+        }
+      } else {
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            amax = fmaxf(amax, fabsf(__uint_as_float(qraw[i][k] << 16)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(qraw[i][k] & 0xffff0000u)));
+          }
+        }
+        amax = max_over_groups(amax);
+        const int e = split_exponent(amax);
+        const float up = __uint_as_float((uint32_t)(127 + e) << 23);
+        if (grp == 0) sm_cs[16 * hh + col] = cscale * __uint_as_float((uint32_t)(127 - e) << 23);
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+          uint64_t hi, lo;
+          split8_bf16_e4m3(qraw[i], up, hi, lo);
+          *reinterpret_cast<uint64_t*>(img + i * 64 * QB) = hi;
+          *reinterpret_cast<uint64_t*>(img + QIMG + i * 64 * QB) = lo;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  float cs[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) cs[hh] = SPLIT ? sm_cs[16 * hh + col] : cscale;
+  auto qop8 = [&](int hh, int i, bool lo) __attribute__((always_inline)) -> uint64_t {
+    return *reinterpret_cast<const uint64_t*>(smem + (lo ? QIMG : 0) + (size_t)((hh * NQ + i) * 64 + lane) * QB);
+  };
+  auto qop16 = [&](int hh, int i) __attribute__((always_inline)) -> bf16x8_t {
+    return *reinterpret_cast<const bf16x8_t*>(smem + (size_t)((hh * NQ + i) * 64 + lane) * QB);
+  };
+
+  f32x4_t oacc[2][S::NT];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+    for (int t = 0; t < S::NT; ++t) oacc[hh][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
+
+  // S^T tiles of a unit for both halves: rows = its 16 keys, columns = 16 query rows each
+  auto qk = [&](const u32x4_t (&kk)[S::KCH], f32x4_t (&sacc)[2]) __attribute__((always_inline)) {
+    f32x4_t slo[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) sacc[hh] = slo[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < S::KCH; ++c) {
+      if constexpr (QFP8) {
+        const uint64_t k0 = (uint64_t)kk[c][0] | ((uint64_t)kk[c][1] << 32);
+        const uint64_t k1 = (uint64_t)kk[c][2] | ((uint64_t)kk[c][3] << 32);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          sacc[hh] = mfma_fp8_16x16x32(k0, qop8(hh, 2 * c, false), sacc[hh]);
+          sacc[hh] = mfma_fp8_16x16x32(k1, qop8(hh, 2 * c + 1, false), sacc[hh]);
+          if constexpr (SPLIT) {   // the split accumulation: K hi + (K lo) / 16
+            slo[hh] = mfma_fp8_16x16x32(k0, qop8(hh, 2 * c, true), slo[hh]);
+            slo[hh] = mfma_fp8_16x16x32(k1, qop8(hh, 2 * c + 1, true), slo[hh]);
+          }
+        }
+      } else {
+        const bf16x8_t kb0 = e4m3x8_to_bf16(kk[c][0], kk[c][1]);
+        const bf16x8_t kb1 = e4m3x8_to_bf16(kk[c][2], kk[c][3]);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          sacc[hh] = mfma_bf16_16x16x32(kb0, qop16(hh, 2 * c), sacc[hh]);
+          sacc[hh] = mfma_bf16_16x16x32(kb1, qop16(hh, 2 * c + 1), sacc[hh]);
+        }
+      }
+    }
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) sacc[hh] += slo[hh] * 0.0625f;
+    }
+  };
+
+  // mask, online softmax update and P^T operand of half hh (as in decode_tile)
+  constexpr float kLazy = SPLIT ? 4.0f : kLazyMax;
+  auto softmax = [&](const f32x4_t sacc, int u, int hh) __attribute__((always_inline)) -> f32x4_t {
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = sacc[i] * cs[hh];
+    const int j0 = u * 16;
+    if (!(j0 >= full_lo && j0 + 15 <= p_first)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + 4 * grp + i;
+        const bool vis = j <= pos[hh] && (W < 1 || j > pos[hh] - W);
+        sv[i] = vis ? sv[i] : kNegInf;
+      }
+    }
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = max_over_groups(mx);
+    const bool grow = mx > m_run[hh] + kLazy;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run[hh];
+      const float alpha = fast_exp2(m_run[hh] - (m_new == kNegInf ? 0.f : m_new));
+      l_run[hh] *= alpha;
+      if (__any(grow && m_run[hh] != kNegInf)) {
+#pragma unroll
+        for (int t = 0; t < S::NT; ++t) oacc[hh][t] *= alpha;
+      }
+      m_run[hh] = m_new;
+    }
+    const float m_use = m_run[hh] == kNegInf ? 0.f : m_run[hh];
+    float pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(sv[i] - m_use);
+    l_run[hh] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+    return f32x4_t{pv[0], pv[1], pv[2], pv[3]};
+  };
+
+  // O^T += V^T * P^T for both halves; the V^T operands (byte transpose, dequant) are made once
+  auto compute = [&](const UnitRegs<DP>& ur, int u) __attribute__((always_inline)) {
+    f32x4_t sacc[2];
+    qk(ur.k, sacc);
+    uint64_t p8[2] = {0, 0};
+    bf16x4_t pb[2] = {};
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const f32x4_t pf = softmax(sacc[hh], u, hh);
+      if constexpr (SPLIT) {
+        int hc = __builtin_amdgcn_cvt_pk_fp8_f32(pf[0], pf[1], 0, false);
+        hc = __builtin_amdgcn_cvt_pk_fp8_f32(pf[2], pf[3], hc, true);
+        const f32x2_t h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hc, false);
+        const f32x2_t h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hc, true);
+        int h16 = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * h01[0], 16.0f * h01[1], 0, false);
+        h16 = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * h23[0], 16.0f * h23[1], h16, true);
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * (pf[0] - h01[0]), 16.0f * (pf[1] - h01[1]), 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * (pf[2] - h23[0]), 16.0f * (pf[3] - h23[1]), lo, true);
+        p8[hh] = (uint64_t)(uint32_t)h16 | ((uint64_t)(uint32_t)lo << 32);
+      } else {
+        pb[hh] = bf16x4_t{(__bf16)pf[0], (__bf16)pf[1], (__bf16)pf[2], (__bf16)pf[3]};
+      }
+    }
+#pragma unroll
+    for (int blk = 0; blk < S::VBLK; ++blk) {
+#pragma unroll
+      for (int w = 0; w < S::CW / 4; ++w) {
+        uint32_t tr[4];
+        transpose4x4_u8(ur.v[0][blk][w], ur.v[1][blk][w], ur.v[2][blk][w], ur.v[3][blk][w],
+                        tr[0], tr[1], tr[2], tr[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = blk * S::CW + 4 * w + e;
+          if constexpr (SPLIT) {
+            const uint64_t a = (uint64_t)tr[e] | ((uint64_t)tr[e] << 32);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) oacc[hh][t] = mfma_fp8_16x16x32(a, p8[hh], oacc[hh][t]);
+          } else {
+            const bf16x4_t a = e4m3x4_to_bf16(tr[e]);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) oacc[hh][t] = mfma_bf16_16x16x16(a, pb[hh], oacc[hh][t]);
+          }
+        }
+      }
+    }
+  };
+
+  // ---- main loop: this wave takes units su0+wave, su0+wave+4, ... --------------------------
+  for (int u = u0; u < su1; u += 4 * NBUF) {
+#pragma unroll
+    for (int k = 0; k < NBUF; ++k) {
+      const int uk = u + 4 * k;
+      if (uk < su1) compute(buf[k], uk);
+      issue(buf[k], uk + 4 * NBUF);
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) l_run[hh] = sum_over_groups(l_run[hh]);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the trailing loads land before the block ends
+  __syncthreads();                            // every wave is done with the Q image
+
+  // ---- merge the 4 waves through LDS, one half at a time ------------------------------------
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    if (grp == 0) {
+      sm_m[wave][col] = m_run[hh];
+      sm_l[wave][col] = l_run[hh];
+    }
+    __syncthreads();
+    {
+      const float M = fmaxf(fmaxf(sm_m[0][col], sm_m[1][col]), fmaxf(sm_m[2][col], sm_m[3][col]));
+      const float sc = M == kNegInf ? 0.f : fast_exp2(m_run[hh] - M);
+      float* orow = &sm_o[wave][col][0];
+#pragma unroll
+      for (int blk = 0; blk < S::VBLK; ++blk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int e4 = 0; e4 < S::CW / 4; ++e4) {
+            const int t = blk * S::CW + 4 * e4;
+            const f32x4_t v = {oacc[hh][t][i] * sc, oacc[hh][t + 1][i] * sc, oacc[hh][t + 2][i] * sc,
+                               oacc[hh][t + 3][i] * sc};
+            *reinterpret_cast<f32x4_t*>(orow + blk * 16 * S::CW + (4 * grp + i) * S::CW + 4 * e4) = v;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    {
+      const int row = threadIdx.x & 15;
+      const int part = threadIdx.x >> 4;
+      constexpr int PW = DP / 16;
+      const int rr = row0 + 16 * hh + row;
+      if (rr < nrows && part * PW < D) {
+        float mw[4], M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) { mw[w] = sm_m[w][row]; M = fmaxf(M, mw[w]); }
+        float Ls = 0.f;
+        if (M != kNegInf) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) Ls += sm_l[w][row] * fast_exp2(mw[w] - M);
+        }
+        const int tk = t0 + rr / G;
+        const int hq = h * G + rr % G;
+        const float inv = Ls > 0.f ? vd / (SPLIT ? 16.0f * Ls : Ls) : 0.f;   // (split Q accumulates 16 O)
+        const float lse2 = Ls > 0.f ? (M + fast_log2(Ls)) : kNegInf;
+        if (whole) {
+          __bf16* op = reinterpret_cast<__bf16*>(p.out) + (int64_t)tk * p.out_stride_tok +
+                       (int64_t)hq * p.out_stride_head + part * PW;
+#pragma unroll
+          for (int c = 0; c < PW; c += 4) {
+            f32x4_t a = *reinterpret_cast<const f32x4_t*>(&sm_o[0][row][part * PW + c]);
+#pragma unroll
+            for (int w = 1; w < 4; ++w) a += *reinterpret_cast<const f32x4_t*>(&sm_o[w][row][part * PW + c]);
+            a *= inv;
+            const bf16x4_t o = {(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3]};
+            *reinterpret_cast<bf16x4_t*>(op + c) = o;
+          }
+          if (p.lse && part == 0) p.lse[(int64_t)tk * p.hq + hq] = lse2 * kLn2;
+        } else {
+          const int64_t e = ((int64_t)pidx * p.total_q + tk) * p.hq + hq;   // [split, token, q head]
+          float* op = p.part_o + e * D + part * PW;
+#pragma unroll
+          for (int c = 0; c < PW; c += 4) {
+            f32x4_t a = *reinterpret_cast<const f32x4_t*>(&sm_o[0][row][part * PW + c]);
+#pragma unroll
+            for (int w = 1; w < 4; ++w) a += *reinterpret_cast<const f32x4_t*>(&sm_o[w][row][part * PW + c]);
+            *reinterpret_cast<f32x4_t*>(op + c) = a * inv;
+          }
+          if (part == 0) p.part_lse[e] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;
+        }
+      }
+    }
+    __syncthreads();   // the next half reuses the merge buffers
+  }
+}
+
+// Split grid over 32-row tiles (row_groups counts 32-row tiles here)
+template <int QM, int D>
+__global__ void __launch_bounds__(256) decode32_kernel(const AttnParams p) {
+  uint32_t id = xcd_remap32(blockIdx.x, gridDim.x);
+  const uint32_t n_rt = (uint32_t)p.row_groups, n_b = (uint32_t)p.batch, n_s = (uint32_t)p.num_splits;
+  const int rt = (int)(id % n_rt); id /= n_rt;
+  const int b = (int)(id % n_b); id /= n_b;
+  const int s = (int)(id % n_s);
+  const int h = (int)(id / n_s);
+  const int o0 = s * p.units_per_split;
+  decode_tile32<QM, D>(p, b, h, rt, o0, o0 + p.units_per_split, s, p.num_splits == 1);
+}
+
 // ---- balanced partition ----------------------------------------------------------------------
 // The row tiles' visible 16-key units, laid end to end in (kv head, sequence, row tile) order,
 // form one stream of T units; block i of R = min(grid, T) takes units [i T / R, (i + 1) T / R).
@@ -718,6 +1154,8 @@ static void launch_decode_dims(const AttnParams& p, int head_dim, dim3 g, hipStr
 #define FP8ATTN_DECODE(DIM)                                                                  \
   do {                                                                                       \
     if constexpr (BAL) hipLaunchKernelGGL((decode_balanced_kernel<QM, DIM>), g, blk, 0, stream, p); \
+    else if (DIM <= 256 && p.tile_rows == 32)                                                 \
+      hipLaunchKernelGGL((decode32_kernel<QM, (DIM <= 256 ? DIM : 256)>), g, blk, 0, stream, p); \
     else hipLaunchKernelGGL((decode_kernel<QM, DIM>), g, blk, 0, stream, p);                 \
   } while (0)
   switch (head_dim) {

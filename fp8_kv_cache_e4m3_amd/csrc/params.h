@@ -34,7 +34,8 @@ struct AttnParams {
   // split-KV decode
   int32_t num_splits;                          // S >= 1
   int32_t units_per_split;                     // 16-key units per split
-  int32_t row_groups;                          // 16-row tiles per (sequence, kv head)
+  int32_t row_groups;                          // row tiles per (sequence, kv head)
+  int32_t tile_rows;                           // rows per tile: 16, or 32 (split grid only)
   int32_t max_seqlen_q;
   float* part_o;                               // fp32 [S, total_q, hq, d] when S > 1
   float* part_lse;                             // fp32 [S, total_q, hq]

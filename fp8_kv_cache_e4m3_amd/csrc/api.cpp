@@ -510,6 +510,9 @@ fp8attn_status fp8attn_prefill_varlen(const fp8attn_attn_args* args, hipStream_t
   hipError_t e;
   if ((args->q_dtype == FP8ATTN_E4M3 || args->q_dtype == FP8ATTN_BF16_TO_E4M3) && args->head_dim != 96) {
     e = fp8attn::launch_prefill_fp8(p, args->head_dim, args->q_dtype == FP8ATTN_BF16_TO_E4M3, stream);
+  } else if (args->head_dim == 512) {
+    // the full-attention layers' head dim with bf16 Q: the d512 MFMA prefill
+    e = fp8attn::launch_prefill_wide(p, args->q_dtype == FP8ATTN_BF16_SPLIT, stream);
   } else {
     // BF16 queries, and head dim 96 (whose rows do not split into the prefill tiles' 64-byte
     // k-steps): the split-KV kernel over 32-row query tiles (16 when no sequence has more rows

@@ -141,46 +141,6 @@ struct DecodeTune {
   static constexpr int MIN_WAVES = D == 256 ? 2 : 1;
 };
 
-// Split Q (kQBf16Split): one query row, scaled by a power of two 2^e so that its largest
-// magnitude is at most 448, is written as hi + lo / 16 with hi = E4M3(x 2^e) and
-// lo = E4M3(16 (x 2^e - hi)).  A bf16 value has 8 significant bits; hi keeps the top 4 (rounded
-// to nearest even) and the residual then has at most 4, so hi + lo / 16 equals x 2^e exactly
-// unless hi or lo falls below E4M3's normal range (|x| under about 2^-14 of the row's largest).
-// QK^T is then accumulated in two parts on the FP8 MFMA, S = K hi + (K lo) / 16, and scaled back
-// by 2^-e: the BF16 product up to the order of the fp32 sums.
-__device__ __forceinline__ void split8_bf16_e4m3(const u32x4_t w, const float scale, uint64_t& hi, uint64_t& lo) {
-  float x[8], r[8];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    x[2 * k] = __uint_as_float(w[k] << 16) * scale;           // exact: a power-of-two scale
-    x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u) * scale;
-  }
-  int h[2], l[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    h[q] = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q], x[4 * q + 1], 0, false);
-    h[q] = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q + 2], x[4 * q + 3], h[q], true);
-    const f32x2_t d0 = __builtin_amdgcn_cvt_pk_f32_fp8(h[q], false);
-    const f32x2_t d1 = __builtin_amdgcn_cvt_pk_f32_fp8(h[q], true);
-    r[4 * q] = (x[4 * q] - d0[0]) * 16.0f;                    // exact differences
-    r[4 * q + 1] = (x[4 * q + 1] - d0[1]) * 16.0f;
-    r[4 * q + 2] = (x[4 * q + 2] - d1[0]) * 16.0f;
-    r[4 * q + 3] = (x[4 * q + 3] - d1[1]) * 16.0f;
-    l[q] = __builtin_amdgcn_cvt_pk_fp8_f32(r[4 * q], r[4 * q + 1], 0, false);
-    l[q] = __builtin_amdgcn_cvt_pk_fp8_f32(r[4 * q + 2], r[4 * q + 3], l[q], true);
-  }
-  hi = (uint64_t)(uint32_t)h[0] | ((uint64_t)(uint32_t)h[1] << 32);
-  lo = (uint64_t)(uint32_t)l[0] | ((uint64_t)(uint32_t)l[1] << 32);
-}
-
-// 2^e with e = floor(log2(448 / amax)), clamped to [-126, 126] (both 2^e and 2^-e normal); an
-// all-zero row takes 2^126.
-__device__ __forceinline__ int split_exponent(float amax) {
-  const float m = 448.0f / amax;
-  const int e = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127;
-  return max(-126, min(126, e));
-}
-
 template <bool QFP8, int D>
 struct QRegs;
 template <int D>

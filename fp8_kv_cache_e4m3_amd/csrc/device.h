@@ -223,4 +223,89 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t n) {
   return x * per + (x < rem ? x : rem) + k;
 }
 
+// ---------------------------------------------------------------------------------------------
+// 32x32 FP8 MFMA with operand scales, P packing, LDS operand addressing (the prefill kernels)
+// ---------------------------------------------------------------------------------------------
+constexpr int kE8M0One = 127;        // E8M0 scale 2^0
+constexpr int kE8M0Sixteenth = 123;  // E8M0 scale 2^-4
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16_t mfma_fp8_32x32x64(const i32x8_t& a, const i32x8_t& b, f32x16_t c,
+                                                      int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kE8M0One, 0, scale_b);
+}
+
+// four fp32 -> four E4M3 bytes (round to nearest even; inputs are in [0, 448])
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+// exact decode of the four E4M3 bytes of a dword (only used for the split-P residual)
+__device__ __forceinline__ void unpack4_e4m3(uint32_t w, float out[4]) {
+  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  out[0] = lo[0];
+  out[1] = lo[1];
+  out[2] = hi[0];
+  out[3] = hi[1];
+}
+
+// A per-lane LDS byte offset the optimiser treats as opaque, so that it is not split into a chain
+// of address computations.  Every operand read is then the stage array plus this offset plus a
+// constant, and the LDS lowering can still tell which array (stage) each read touches: that is
+// what lets a read of one stage proceed while direct-to-LDS loads into another are in flight.
+__device__ __forceinline__ int lane_offset(int x) {
+  asm("" : "+v"(x));
+  return x;
+}
+
+// MFMA row m of a 32-key half tile holds key kperm(m): bits 2 and 3 of m swapped.
+__device__ __forceinline__ int kperm(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// ---------------------------------------------------------------------------------------------
+// Split Q: bf16 values as two E4M3 terms (the decode and d512 prefill kernels)
+// ---------------------------------------------------------------------------------------------
+// Split Q (kQBf16Split): one query row, scaled by a power of two 2^e so that its largest
+// magnitude is at most 448, is written as hi + lo / 16 with hi = E4M3(x 2^e) and
+// lo = E4M3(16 (x 2^e - hi)).  A bf16 value has 8 significant bits; hi keeps the top 4 (rounded
+// to nearest even) and the residual then has at most 4, so hi + lo / 16 equals x 2^e exactly
+// unless hi or lo falls below E4M3's normal range (|x| under about 2^-14 of the row's largest).
+// QK^T is then accumulated in two parts on the FP8 MFMA, S = K hi + (K lo) / 16, and scaled back
+// by 2^-e: the BF16 product up to the order of the fp32 sums.
+__device__ __forceinline__ void split8_bf16_e4m3(const u32x4_t w, const float scale, uint64_t& hi, uint64_t& lo) {
+  float x[8], r[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(w[k] << 16) * scale;           // exact: a power-of-two scale
+    x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u) * scale;
+  }
+  int h[2], l[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    h[q] = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q], x[4 * q + 1], 0, false);
+    h[q] = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q + 2], x[4 * q + 3], h[q], true);
+    const f32x2_t d0 = __builtin_amdgcn_cvt_pk_f32_fp8(h[q], false);
+    const f32x2_t d1 = __builtin_amdgcn_cvt_pk_f32_fp8(h[q], true);
+    r[4 * q] = (x[4 * q] - d0[0]) * 16.0f;                    // exact differences
+    r[4 * q + 1] = (x[4 * q + 1] - d0[1]) * 16.0f;
+    r[4 * q + 2] = (x[4 * q + 2] - d1[0]) * 16.0f;
+    r[4 * q + 3] = (x[4 * q + 3] - d1[1]) * 16.0f;
+    l[q] = __builtin_amdgcn_cvt_pk_fp8_f32(r[4 * q], r[4 * q + 1], 0, false);
+    l[q] = __builtin_amdgcn_cvt_pk_fp8_f32(r[4 * q + 2], r[4 * q + 3], l[q], true);
+  }
+  hi = (uint64_t)(uint32_t)h[0] | ((uint64_t)(uint32_t)h[1] << 32);
+  lo = (uint64_t)(uint32_t)l[0] | ((uint64_t)(uint32_t)l[1] << 32);
+}
+
+// 2^e with e = floor(log2(448 / amax)), clamped to [-126, 126] (both 2^e and 2^-e normal); an
+// all-zero row takes 2^126.
+__device__ __forceinline__ int split_exponent(float amax) {
+  const float m = 448.0f / amax;
+  const int e = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127;
+  return max(-126, min(126, e));
+}
+
 }  // namespace fp8attn

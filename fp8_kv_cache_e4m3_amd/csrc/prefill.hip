@@ -36,46 +36,8 @@
 
 namespace fp8attn {
 
-typedef int i32x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
 constexpr int kSplitPKeys = 512;
-constexpr int kE8M0One = 127;        // E8M0 scale 2^0
-constexpr int kE8M0Sixteenth = 123;  // E8M0 scale 2^-4
 constexpr float kLazyMax = 8.0f;
-
-__device__ __forceinline__ f32x16_t mfma_fp8_32x32x64(const i32x8_t& a, const i32x8_t& b, f32x16_t c,
-                                                      int scale_b) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kE8M0One, 0, scale_b);
-}
-
-// four fp32 -> four E4M3 bytes (round to nearest even; inputs are in [0, 448])
-__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return (uint32_t)w;
-}
-// exact decode of the four E4M3 bytes of a dword (only used for the split-P residual)
-__device__ __forceinline__ void unpack4_e4m3(uint32_t w, float out[4]) {
-  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  out[0] = lo[0];
-  out[1] = lo[1];
-  out[2] = hi[0];
-  out[3] = hi[1];
-}
-
-// A per-lane LDS byte offset the optimiser treats as opaque, so that it is not split into a chain
-// of address computations.  Every operand read is then the stage array plus this offset plus a
-// constant, and the LDS lowering can still tell which array (stage) each read touches: that is
-// what lets a read of one stage proceed while direct-to-LDS loads into another are in flight.
-__device__ __forceinline__ int lane_offset(int x) {
-  asm("" : "+v"(x));
-  return x;
-}
-
-// MFMA row m of a 32-key half tile holds key kperm(m): bits 2 and 3 of m swapped.
-__device__ __forceinline__ int kperm(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 template <int D>
 struct PrefillShape {

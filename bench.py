@@ -426,6 +426,8 @@ def main():
                     choices=["swa_decode", "full_decode", "spec_verify", "swa_prefill", "full_prefill",
                              "kv_write_swa_prefill"],
                     help="short run for rocprofv3 counter passes: one workload plus a 1 GiB device copy")
+    ap.add_argument("--split-q", action="store_true",
+                    help="with --profile-pass on a bf16-Q workload: q_dtype BF16_SPLIT (QK^T and PV on the FP8 MFMA)")
     ap.add_argument("--separate-quantize", action="store_true",
                     help="quantize Q with its own call before attention (two launches per step) instead of "
                          "inside the attention kernel")
@@ -463,7 +465,8 @@ def main():
             time_cache_write(lambda s: wl.swa_prefill(device="cuda", seed=400 + s), args.steps, "kv_write (profile pass)")
             return
         make, entry = makers[args.profile_pass]
-        time_workload(make, entry, 2, args.steps, args.warmup, f"{args.profile_pass} (profile pass)", fused)
+        time_workload(make, entry, 2, args.steps, args.warmup, f"{args.profile_pass} (profile pass)", fused,
+                      args.split_q)
         return
 
     main = time_workload(lambda s: wl.swa_decode(device="cuda", seed=100 + s), "decode", nsets, args.steps,

@@ -15,15 +15,17 @@
 //  * A block owns 64 query rows of one (sequence, kv head), rows token-major as in the other
 //    kernels; each wave owns 16 rows (the MFMA's column count), so its O^T (512 d x 16 rows, fp32)
 //    takes 128 accumulation registers and its Q 64 registers.
-//  * K and V arrive one 64-key tile at a time straight into LDS (buffer loads with an LDS
+//  * K and V arrive one 32-key tile at a time straight into LDS (buffer loads with an LDS
 //    destination, range ending at the sequence length so rows past it read zeros), in a ring of
-//    two stages of 2 x 64 x 528 bytes; key rows are padded to 528 bytes (a copy of the row's first
-//    16 bytes), which spreads the 16 key rows of an operand read over distinct banks.
+//    four stages; key rows are padded to 528 bytes (a copy of the row's first 16 bytes), which
+//    spreads the 16 key rows of an operand read over distinct banks.  Tile t + 3 is requested
+//    while tile t is computed, so a tile's loads have two tiles of compute to land: with two
+//    stages of 64-key tiles (all the LDS holds at this head dim) the wait for the next tile took
+//    a third of the time.  One barrier per tile.
 //  * S^T = K Q^T with keys on the MFMA rows and query rows on the columns, so a row's softmax state
-//    is per lane.  MFMA row m of 16-key block kb holds key 32 (kb / 2) + 8 (m / 4) + 4 (kb % 2) +
-//    m % 4: then the 8 keys whose P a lane group feeds to one PV MFMA are 8 consecutive keys, and
-//    one transposing LDS read (ds_read_b64_tr_b8) gives the matching V^T operand.
-//  * Two barriers per tile: one before a stage is refilled, one after its next tile has landed.
+//    is per lane.  MFMA row m of 16-key block kb holds key 8 (m / 4) + 4 kb + m % 4: then the 8
+//    keys whose P a lane group feeds to one PV MFMA are 8 consecutive keys, and one transposing LDS
+//    read (ds_read_b64_tr_b8) gives the matching V^T operand.
 #include <type_traits>
 
 #include "device.h"
@@ -34,16 +36,19 @@ namespace fp8attn {
 namespace {
 
 constexpr int kD = 512;
-constexpr int kNW = 4;                    // waves per block
+constexpr int kNW = 8;                    // waves per block (two per SIMD)
 constexpr int kRW = 16;                   // rows per wave
 constexpr int kBM = kNW * kRW;            // rows per block
-constexpr int kBK = 64;                   // keys per tile
+constexpr int kBK = 32;                   // keys per tile
+constexpr int kNS = 4;                    // stages in the LDS ring
 constexpr int kNCH = kD / 16;             // 16-byte chunks per key row
 constexpr int kRS = kD + 16;              // LDS row stride (one pad slot)
 constexpr int kSlots = kNCH + 1;          // 16-byte LDS slots per key row
-constexpr int kTile = kBK * kRS;          // bytes of one K (or V) tile
+constexpr int kRowSlots = kBK * kSlots;   // 1,056 slots of key rows per tile ...
+constexpr int kInsPerTile = (kRowSlots + 63) / 64;   // ... written by 17 wave-wide loads
+constexpr int kTile = kInsPerTile * 1024; // bytes of one K (or V) tile: rows, then 32 spare slots
 constexpr int kStage = 2 * kTile;         // [K tile | V tile]
-constexpr int kLoads = 2 * kSlots;        // wave-wide 1 KiB loads per K+V tile
+constexpr int kLoads = 2 * kInsPerTile;   // wave-wide 1 KiB loads per K+V tile
 constexpr int kMaxI = (kLoads + kNW - 1) / kNW;   // loads per wave per tile
 constexpr int kNT = kD / 16;              // O^T tiles of 16 d rows
 
@@ -59,14 +64,12 @@ __device__ __forceinline__ int wide_load_instruction(int wave, int k) {
 }
 
 // key of MFMA row m in 16-key block kb of a tile
-__device__ __forceinline__ int block_key(int kb, int m) {
-  return 32 * (kb >> 1) + 8 * (m >> 2) + 4 * (kb & 1) + (m & 3);
-}
+__device__ __forceinline__ int block_key(int kb, int m) { return 8 * (m >> 2) + 4 * kb + (m & 3); }
 
 }  // namespace
 
 template <bool SPLITQ>
-__global__ void __launch_bounds__(256) prefill_wide_kernel(const AttnParams p, int32_t qb_end,
+__global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) prefill_wide_kernel(const AttnParams p, int32_t qb_end,
                                                            const int32_t* __restrict__ block_table) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -120,7 +123,7 @@ __global__ void __launch_bounds__(256) prefill_wide_kernel(const AttnParams p, i
   float cs = p.scale_log2 * kd;      // (split Q: times the row's 2^-e)
 
   // ---- LDS ring and tile loads ---------------------------------------------------------------
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kNS * kStage];
   const uint32_t lds_base = lds_address(lds);
   const int32_t* bt = block_table + (int64_t)b * p.bt_stride;
   const uint8_t* kbase = p.k_cache + (int64_t)h * p.kv_stride_head;
@@ -128,7 +131,8 @@ __global__ void __launch_bounds__(256) prefill_wide_kernel(const AttnParams p, i
   const int64_t sT = p.kv_stride_tok, sP = p.kv_stride_page;
   const int ps = p.page_size;
   // This wave's loads of tile kt into stage st: a wave-wide instruction fills 64 consecutive
-  // 16-byte slots; key rows take kSlots slots, the last one a copy of the row's first chunk.  The
+  // 16-byte slots; key rows take kSlots slots, the last one a copy of the row's first chunk, and
+  // the slots past the rows (the last instruction's second half) get the tile's first chunk.  The
   // buffers' range ends with the tile's last key below L: rows past it read zeros (slots never
   // written for this sequence, possibly holding NaN codes, which 0 * NaN in the MFMA would spread).
   // idle: a load past the block's last tile, which only keeps the count of loads per tile fixed;
@@ -145,15 +149,16 @@ __global__ void __launch_bounds__(256) prefill_wide_kernel(const AttnParams p, i
 #pragma unroll
     for (int k = 0; k < kMaxI; ++k) {
       const int ins = wide_load_instruction(wave, k);
-      const int which = ins / kSlots, blk = ins % kSlots;
+      const int which = ins / kInsPerTile, blk = ins % kInsPerTile;
       const int sl = blk * 64 + ln;
       const int row = sl / kSlots, posn = sl % kSlots;
-      const uint32_t voff = idle ? 0u : (uint32_t)(row * sT) + 16u * (uint32_t)(posn == kNCH ? 0 : posn);
+      const uint32_t voff = idle || sl >= kRowSlots ? 0u : (uint32_t)(row * sT) + 16u * (uint32_t)(posn == kNCH ? 0 : posn);
       lds_dma16_buf(which ? vrs : krs, voff, so + (uint32_t)(which * kTile + blk * 1024));
     }
   };
   issue(0, kt0, false);
   issue(1, min(kt0 + 1, kt1), kt0 + 1 > kt1);
+  issue(2, min(kt0 + 2, kt1), kt0 + 2 > kt1);
 
   // ---- Q^T operands ---------------------------------------------------------------------------
   // BF16: per 32-d step c, lane (row col, group grp) holds Q[row][32 c + 8 grp .. + 7].
@@ -209,29 +214,29 @@ __global__ void __launch_bounds__(256) prefill_wide_kernel(const AttnParams p, i
   for (int t = 0; t < kNT; ++t) oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
 
-  // per-lane LDS offsets: the K row of each 16-key block for the S^T A operand (blocks 0/1 and 2/3
-  // differ by 32 rows), and the V^T transposing reads (this lane supplies source row j = col / 2,
-  // 8-byte half col % 2; its group reads keys 8 grp .. 8 grp + 7 of a 32-key half)
+  // per-lane LDS offsets: the K row of each 16-key block for the S^T A operand, and the V^T
+  // transposing reads (this lane supplies source row j = col / 2, 8-byte half col % 2; its group
+  // reads keys 8 grp .. 8 grp + 7 of the tile)
   const int k_lane0 = lane_offset(block_key(0, col) * kRS + (SPLITQ ? 32 : 8) * grp);
   const int k_lane1 = lane_offset(block_key(1, col) * kRS + (SPLITQ ? 32 : 8) * grp);
   const int v_lane = lane_offset((8 * grp + (col >> 1)) * kRS + 8 * (col & 1));
 
-  // S^T = K Q^T of the tile in stage st, four 16-key blocks.  Operands stream in two MFMAs ahead of
+  // S^T = K Q^T of the tile in stage st, two 16-key blocks.  Operands stream in two MFMAs ahead of
   // their use through a ring of three registers (fixed by scheduling barriers).
-  //   BF16: op j = (32-d step j / 4, block j % 4), K bytes converted exactly to bf16.
-  //   Split: op j = (128-d step j / 4, block j % 4), the MFMA pair K hi + (K lo) 2^-4.
+  //   BF16: op j = (32-d step j / 2, block j % 2), K bytes converted exactly to bf16.
+  //   Split: op j = (128-d step j / 2, block j % 2), the MFMA pair K hi + (K lo) 2^-4.
   typedef typename std::conditional<SPLITQ, i32x8_t, bf16x8_t>::type kop_t;
-  auto qk = [&](int st, f32x4_t (&sacc)[4]) __attribute__((always_inline)) {
+  auto qk = [&](int st, f32x4_t (&sacc)[2]) __attribute__((always_inline)) {
     const uint8_t* kst = lds + st * kStage;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) sacc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    constexpr int NOPS = 4 * NQ;
+    for (int kb = 0; kb < 2; ++kb) sacc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    constexpr int NOPS = 2 * NQ;
     kop_t buf[3];
 #pragma unroll
     for (int j = 0; j < NOPS + 2; ++j) {
       if (j < NOPS) {
-        const int kb = j & 3, c = j >> 2;
-        const uint8_t* kp = kst + ((kb & 1) ? k_lane1 : k_lane0) + 32 * (kb >> 1) * kRS;
+        const int kb = j & 1, c = j >> 1;
+        const uint8_t* kp = kst + (kb ? k_lane1 : k_lane0);
         if constexpr (SPLITQ) {
           const u32x4_t x = *reinterpret_cast<const u32x4_t*>(kp + 128 * c);
           const u32x4_t y = *reinterpret_cast<const u32x4_t*>(kp + 128 * c + 16);
@@ -243,7 +248,7 @@ __global__ void __launch_bounds__(256) prefill_wide_kernel(const AttnParams p, i
       }
       __builtin_amdgcn_sched_barrier(0);
       if (j >= 2) {
-        const int i = j - 2, kb = i & 3, c = i >> 2;
+        const int i = j - 2, kb = i & 1, c = i >> 1;
         if constexpr (SPLITQ) {
           sacc[kb] = mfma_fp8_16x16x128(buf[i % 3], qhi[c], sacc[kb], kE8M0One);
           sacc[kb] = mfma_fp8_16x16x128(buf[i % 3], qlo[c], sacc[kb], kE8M0Sixteenth);
@@ -257,27 +262,27 @@ __global__ void __launch_bounds__(256) prefill_wide_kernel(const AttnParams p, i
 
   // softmax of tile kt: mask (boundary tiles), lazy max, O rescale, running sum, P operands.
   // S^T value i of block kb in this lane is row 4 grp + i, i.e. key block_key(kb, 4 grp + i)
-  // = 32 (kb / 2) + 8 grp + 4 (kb % 2) + i of the tile.
-  // BF16: the P^T operand of 32-key half kh is P of keys 32 kh + 8 grp + 0..7, as bf16.
+  // = 8 grp + 4 kb + i of the tile.
+  // BF16: the P^T operand is P of keys 8 grp + 0..7, as bf16.
   // Split: P <= 2^4 (lazy max at 2^4) and block kb's operand is 16 hi in bytes 0-3 and lo in bytes
-  // 4-7 for keys 32 (kb / 2) + 8 grp + 4 (kb % 2) + 0..3, with hi = E4M3(P), lo = E4M3(16 (P - hi)).
+  // 4-7 for keys 8 grp + 4 kb + 0..3, with hi = E4M3(P), lo = E4M3(16 (P - hi)).
   constexpr float kLazy = SPLITQ ? 4.0f : 8.0f;
-  bf16x8_t pb16[2];
-  uint64_t p8[4];
-  auto softmax = [&](int kt, f32x4_t (&sacc)[4]) __attribute__((always_inline)) {
-    float sv[4][4];
+  bf16x8_t pb16;
+  uint64_t p8[2];
+  auto softmax = [&](int kt, f32x4_t (&sacc)[2]) __attribute__((always_inline)) {
+    float sv[2][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sv[kb][i] = sacc[kb][i] * cs;
     }
     const int j0 = kt * kBK;
     if (!(j0 >= wfull_lo && j0 + kBK - 1 <= wpf)) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int j = j0 + 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + i;
+          const int j = j0 + 8 * grp + 4 * kb + i;
           const bool vis = j <= pos && (W < 1 || j > pos - W);
           sv[kb][i] = vis ? sv[kb][i] : kNegInf;
         }
@@ -285,7 +290,7 @@ __global__ void __launch_bounds__(256) prefill_wide_kernel(const AttnParams p, i
     }
     float mx = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) mx = fmaxf(mx, fmaxf(fmaxf(sv[kb][0], sv[kb][1]), fmaxf(sv[kb][2], sv[kb][3])));
+    for (int kb = 0; kb < 2; ++kb) mx = fmaxf(mx, fmaxf(fmaxf(sv[kb][0], sv[kb][1]), fmaxf(sv[kb][2], sv[kb][3])));
     mx = max_over_groups(mx);
     const bool grow = mx > m_run + kLazy;
     if (__any(grow)) {
@@ -300,7 +305,7 @@ __global__ void __launch_bounds__(256) prefill_wide_kernel(const AttnParams p, i
     }
     const float m_use = m_run == kNegInf ? 0.f : m_run;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
       float pv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(sv[kb][i] - m_use);
@@ -317,38 +322,37 @@ __global__ void __launch_bounds__(256) prefill_wide_kernel(const AttnParams p, i
         p8[kb] = (uint64_t)(uint32_t)h16 | ((uint64_t)(uint32_t)lo << 32);
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pb16[kb >> 1][4 * (kb & 1) + i] = (__bf16)pv[i];
+        for (int i = 0; i < 4; ++i) pb16[4 * kb + i] = (__bf16)pv[i];
       }
     }
   };
 
-  // O^T += V^T P^T with the V tile in stage st.  Transposing read (d tile t, half kh) gives this
-  // lane, for d row 16 t + col, the 8 keys 32 kh + 8 grp + 0..7.  O^T tile t, lane (col, grp) holds
-  // d = 16 t + 4 grp + i of row col.  Operands stream two MFMAs ahead as in qk.
-  //   BF16: op j = (d tile j / 2, half j % 2): one MFMA with the 8 keys as bf16.
-  //   Split: op j = (d tile j / 2, half j % 2): two MFMAs, keys 0-3 and 4-7 of the 8, each with
-  //   its 4 V bytes twice (against 16 hi and lo of P).
+  // O^T += V^T P^T with the V tile in stage st.  Transposing read t gives this lane, for d row
+  // 16 t + col, the 8 keys 8 grp + 0..7.  O^T tile t, lane (col, grp) holds d = 16 t + 4 grp + i of
+  // row col.  Operands stream two MFMAs ahead as in qk.
+  //   BF16: op t: one MFMA with the 8 keys as bf16.
+  //   Split: op t: two MFMAs, keys 0-3 and 4-7 of the 8, each with its 4 V bytes twice (against
+  //   16 hi and lo of P).
   auto pv = [&](int st) __attribute__((always_inline)) {
     const uint8_t* vp = lds + (st * kStage + kTile + v_lane);
-    constexpr int NOPS = 2 * kNT;
+    constexpr int NOPS = kNT;
     uint64_t buf[3];
 #pragma unroll
     for (int j = 0; j < NOPS + 2; ++j) {
       if (j < NOPS) {
-        const int t = j >> 1, kh = j & 1;
-        const i32x2_t v2 = lds_read_tr8(vp + (32 * kh * kRS + 16 * t));
+        const i32x2_t v2 = lds_read_tr8(vp + 16 * j);
         buf[j % 3] = (uint64_t)(uint32_t)v2[0] | ((uint64_t)(uint32_t)v2[1] << 32);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (j >= 2) {
-        const int i = j - 2, t = i >> 1, kh = i & 1;
-        const uint64_t v8 = buf[i % 3];
+        const int t = j - 2;
+        const uint64_t v8 = buf[t % 3];
         if constexpr (SPLITQ) {
           const uint64_t lo4 = v8 & 0xffffffffull, hi4 = v8 >> 32;
-          oacc[t] = mfma_fp8_16x16x32(lo4 | (lo4 << 32), p8[2 * kh], oacc[t]);
-          oacc[t] = mfma_fp8_16x16x32(hi4 | (hi4 << 32), p8[2 * kh + 1], oacc[t]);
+          oacc[t] = mfma_fp8_16x16x32(lo4 | (lo4 << 32), p8[0], oacc[t]);
+          oacc[t] = mfma_fp8_16x16x32(hi4 | (hi4 << 32), p8[1], oacc[t]);
         } else {
-          oacc[t] = mfma_bf16_16x16x32(e4m3x8_to_bf16((uint32_t)v8, (uint32_t)(v8 >> 32)), pb16[kh], oacc[t]);
+          oacc[t] = mfma_bf16_16x16x32(e4m3x8_to_bf16((uint32_t)v8, (uint32_t)(v8 >> 32)), pb16, oacc[t]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -356,20 +360,21 @@ __global__ void __launch_bounds__(256) prefill_wide_kernel(const AttnParams p, i
   };
 
   // ---- main loop -------------------------------------------------------------------------------
+  // Tile x lives in stage (x - kt0) mod 4.  At the end of iteration t every wave has computed tile
+  // t, so in iteration t + 1 the stage of tile t takes tile t + 4.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();                     // tiles kt0 and kt0 + 1 are in LDS
+  __syncthreads();                     // tiles kt0 .. kt0 + 2 are in LDS
   for (int t = kt0; t <= kt1; ++t) {
-    const int st = (t - kt0) & 1;
+    const int st = (t - kt0) & (kNS - 1);
     if (t >= wt0 && t <= wt1) {        // a tile none of this wave's rows sees adds nothing
-      f32x4_t sacc[4];
+      f32x4_t sacc[2];
       qk(st, sacc);
       softmax(t, sacc);
       pv(st);
     }
-    __syncthreads();                   // every wave is done with stage st
-    issue(st, min(t + 2, kt1), t + 2 > kt1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMaxI));   // tile t + 1 has landed (this wave's part)
-    __syncthreads();                   // ... and every wave's part
+    issue((st + 3) & (kNS - 1), min(t + 3, kt1), t + 3 > kt1);   // into the stage of tile t - 1
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kMaxI));   // tile t + 1 has landed (this wave's part)
+    __syncthreads();                   // ... every wave's part, and every wave is done with tile t
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // nothing may land after the block ends
 
@@ -377,7 +382,7 @@ __global__ void __launch_bounds__(256) prefill_wide_kernel(const AttnParams p, i
   l_run = sum_over_groups(l_run);
   const float inv = l_run > 0.f ? vd / (SPLITQ ? 16.0f * l_run : l_run) : 0.f;   // (split P accumulates 16 O)
   constexpr int ORS = 2 * kD + 16;                  // LDS row stride of the staged O (bytes)
-  static_assert(kNW * kRW * ORS <= 2 * kStage, "the staged O fits the stage ring");
+  static_assert(kNW * kRW * ORS <= kNS * kStage, "the staged O fits the stage ring");
   __syncthreads();
   uint8_t* const ow = lds + wave * (kRW * ORS);
 #pragma unroll
@@ -410,10 +415,10 @@ hipError_t launch_prefill_wide(const AttnParams& p, bool split_q, hipStream_t st
   const int64_t grid = nqb * p.hkv * p.batch;
   if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidConfiguration;
   if (split_q)
-    hipLaunchKernelGGL(prefill_wide_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, p, (int32_t)nqb,
+    hipLaunchKernelGGL(prefill_wide_kernel<true>, dim3((unsigned)grid), dim3(kNW * 64), 0, stream, p, (int32_t)nqb,
                        p.block_table);
   else
-    hipLaunchKernelGGL(prefill_wide_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, p, (int32_t)nqb,
+    hipLaunchKernelGGL(prefill_wide_kernel<false>, dim3((unsigned)grid), dim3(kNW * 64), 0, stream, p, (int32_t)nqb,
                        p.block_table);
   return hipGetLastError();
 }

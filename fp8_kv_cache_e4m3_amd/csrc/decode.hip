@@ -320,7 +320,7 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
     const int uc = trailing ? ulast : u;
     const int64_t unit = page_of(uc) * sP + (int64_t)((uc * 16) % ps) * sT;
     // the unit's keys below L (at least one: uc * 16 <= p_last < L)
-    const uint32_t nrec = (uint32_t)min(16, L - uc * 16) * (uint32_t)sT;
+    const uint32_t nrec = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(16, L - uc * 16))) * (uint32_t)sT;
     UnitOffsets o = uoff;
     o.k = trailing ? 0u : o.k;
 #pragma unroll
@@ -679,7 +679,7 @@ __device__ __forceinline__ void decode_tile32(const AttnParams& p, const int b, 
     const bool trailing = u > ulast;
     const int uc = trailing ? ulast : u;
     const int64_t unit = page_of(uc) * sP + (int64_t)((uc * 16) % ps) * sT;
-    const uint32_t nrec = (uint32_t)min(16, L - uc * 16) * (uint32_t)sT;
+    const uint32_t nrec = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(16, L - uc * 16))) * (uint32_t)sT;
     UnitOffsets o = uoff;
     o.k = trailing ? 0u : o.k;
 #pragma unroll

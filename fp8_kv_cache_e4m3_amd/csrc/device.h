@@ -232,6 +232,10 @@ constexpr int kE8M0Sixteenth = 123;  // E8M0 scale 2^-4
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+// 16x16x128 FP8 MFMA with a scale on the B operand (unit scale on A)
+__device__ __forceinline__ f32x4_t mfma_fp8_16x16x128(const i32x8_t& a, const i32x8_t& b, f32x4_t c, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kE8M0One, 0, scale_b);
+}
 __device__ __forceinline__ f32x16_t mfma_fp8_32x32x64(const i32x8_t& a, const i32x8_t& b, f32x16_t c,
                                                       int scale_b) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kE8M0One, 0, scale_b);

@@ -85,7 +85,7 @@ hipError_t launch_decode(const AttnParams& p, int q_mode, int head_dim, int64_t 
 hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, bool q_bf16, hipStream_t stream);
 
 // Prefill at head dim 512 with bf16 Q (q mode kQBf16 or, split_q, kQBf16Split): 128 query rows per
-// block, 64-key tiles through LDS, both contractions on the MFMA.
+// block, 32-key tiles through LDS, both contractions on the MFMA.
 hipError_t launch_prefill_wide(const AttnParams& p, bool split_q, hipStream_t stream);
 
 hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t S, int64_t total_q,

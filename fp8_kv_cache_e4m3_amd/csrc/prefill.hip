@@ -185,7 +185,8 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   const int pf = L - ql + r0 / G;           // first row's position
   const int pl = L - ql + rlast / G;        // last row's position
   const int k_lo = W >= 1 ? max(0, pf - W + 1) : 0;
-  const int kt0 = k_lo / S::BK, kt1 = pl / S::BK;   // inclusive tile range of the block
+  // inclusive tile range of the block (at least tile kt0, also when lengths break the contract)
+  const int kt0 = k_lo / S::BK, kt1 = max(kt0, pl / S::BK);
 
   // this wave's rows and key range
   const int wr0 = r0 + wave * S::RW;
@@ -273,7 +274,7 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   auto issue = [&](int so, int kt, int page, bool idle = false) __attribute__((always_inline)) {
     const int slot0 = ps == S::BK ? 0 : kt * S::BK - ((kt * S::BK) / ps) * ps;
     const int64_t tile_off = (int64_t)page * sP + (int64_t)slot0 * sT;
-    const uint32_t nrec = (uint32_t)min(S::BK, L - kt * S::BK) * (uint32_t)sT;
+    const uint32_t nrec = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(S::BK, L - kt * S::BK))) * (uint32_t)sT;
     const TileLoad tl{buffer_rsrc(kbase + tile_off, nrec), buffer_rsrc(vbase + tile_off, nrec),
                       lds_base + (uint32_t)so};
 #pragma unroll

@@ -11,17 +11,18 @@
 //     no dequantization at all (vLLM PR #60372, review thread: the d512 FP8-MMA kernel keeps BF16
 //     queries and builds a split QK accumulation).
 //
-// Design (gfx950, wave64, 256 threads = 4 waves, one per SIMD):
-//  * A block owns 64 query rows of one (sequence, kv head), rows token-major as in the other
+// Design (gfx950, wave64, 512 threads = 8 waves, two per SIMD):
+//  * A block owns 128 query rows of one (sequence, kv head), rows token-major as in the other
 //    kernels; each wave owns 16 rows (the MFMA's column count), so its O^T (512 d x 16 rows, fp32)
 //    takes 128 accumulation registers and its Q 64 registers.
 //  * K and V arrive one 32-key tile at a time straight into LDS (buffer loads with an LDS
 //    destination, range ending at the sequence length so rows past it read zeros), in a ring of
 //    four stages; key rows are padded to 528 bytes (a copy of the row's first 16 bytes), which
-//    spreads the 16 key rows of an operand read over distinct banks.  Tile t + 3 is requested
-//    while tile t is computed, so a tile's loads have two tiles of compute to land: with two
-//    stages of 64-key tiles (all the LDS holds at this head dim) the wait for the next tile took
-//    a third of the time.  One barrier per tile.
+//    spreads the 16 key rows of an operand read over distinct banks.  A tile is requested two
+//    barriers before it is first read: with two stages of 64-key tiles (all the LDS holds at this
+//    head dim) the wait for the next tile took a third of the time.  One barrier per tile.
+//  * The two waves of a SIMD run half a tile apart (waves 0-3 against 4-7), so one's softmax runs
+//    on the VALU while the other's MFMAs run.
 //  * S^T = K Q^T with keys on the MFMA rows and query rows on the columns, so a row's softmax state
 //    is per lane.  MFMA row m of 16-key block kb holds key 8 (m / 4) + 4 kb + m % 4: then the 8
 //    keys whose P a lane group feeds to one PV MFMA are 8 consecutive keys, and one transposing LDS
@@ -30,6 +31,7 @@
 
 #include "device.h"
 #include "params.h"
+
 
 namespace fp8attn {
 
@@ -51,10 +53,6 @@ constexpr int kStage = 2 * kTile;         // [K tile | V tile]
 constexpr int kLoads = 2 * kInsPerTile;   // wave-wide 1 KiB loads per K+V tile
 constexpr int kMaxI = (kLoads + kNW - 1) / kNW;   // loads per wave per tile
 constexpr int kNT = kD / 16;              // O^T tiles of 16 d rows
-
-__device__ __forceinline__ f32x4_t mfma_fp8_16x16x128(const i32x8_t& a, const i32x8_t& b, f32x4_t c, int scale_b) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kE8M0One, 0, scale_b);
-}
 
 // load instruction k of this wave: instructions w, w + 4, ...; a wave with one fewer repeats its
 // previous one (the same bytes to the same place), so every wave issues the same count
@@ -101,7 +99,7 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2
   const int pf = L - ql + r0 / G;
   const int pl = L - ql + rlast / G;
   const int k_lo = W >= 1 ? max(0, pf - W + 1) : 0;
-  const int kt0 = k_lo / kBK, kt1 = pl / kBK;
+  const int kt0 = k_lo / kBK, kt1 = max(kt0, pl / kBK);   // (one tile at least, also for bad lengths)
 
   // this wave's rows and the tiles some row of it sees
   const int wr0 = r0 + wave * kRW;
@@ -142,7 +140,7 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2
     const int page = bt[ps == kBK ? kt : (kt * kBK) / ps];
     const int slot0 = ps == kBK ? 0 : kt * kBK - ((kt * kBK) / ps) * ps;
     const int64_t tile_off = (int64_t)page * sP + (int64_t)slot0 * sT;
-    const uint32_t nrec = (uint32_t)min(kBK, L - kt * kBK) * (uint32_t)sT;
+    const uint32_t nrec = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(kBK, L - kt * kBK))) * (uint32_t)sT;
     const i32x4_t krs = buffer_rsrc(kbase + tile_off, nrec), vrs = buffer_rsrc(vbase + tile_off, nrec);
     const uint32_t so = lds_base + (uint32_t)(st * kStage);
     const int ln = lane_offset(lane);
@@ -213,6 +211,8 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
   for (int t = 0; t < kNT; ++t) oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
+  float o_scale = 1.f;                 // pending rescale of O (lazy max moved), per row
+  bool o_rescale = false;              // ... for some row of the wave
 
   // per-lane LDS offsets: the K row of each 16-key block for the S^T A operand, and the V^T
   // transposing reads (this lane supplies source row j = col / 2, 8-byte half col % 2; its group
@@ -298,12 +298,13 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2
       const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));   // 1 where not grown
       l_run *= alpha;
       if (__any(grow && m_run != kNegInf)) {
-#pragma unroll
-        for (int t = 0; t < kNT; ++t) oacc[t] *= alpha;
+        o_scale *= alpha;              // applied to O before the tile's PV
+        o_rescale = true;
       }
       m_run = m_new;
     }
     const float m_use = m_run == kNegInf ? 0.f : m_run;
+    float pall[8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float pv[4];
@@ -322,9 +323,16 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2
         p8[kb] = (uint64_t)(uint32_t)h16 | ((uint64_t)(uint32_t)lo << 32);
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pb16[4 * kb + i] = (__bf16)pv[i];
+        for (int i = 0; i < 4; ++i) pall[4 * kb + i] = pv[i];
       }
     }
+    if constexpr (!SPLITQ)
+      pb16 = bf16x8_t{(__bf16)pall[0], (__bf16)pall[1], (__bf16)pall[2], (__bf16)pall[3],
+                      (__bf16)pall[4], (__bf16)pall[5], (__bf16)pall[6], (__bf16)pall[7]};
+    // P and the running sum are needed here: the compiler would otherwise sink the exponentials
+    // past the barrier that may follow, into the MFMA half of the interval
+    if constexpr (SPLITQ) asm volatile("" ::"v"(p8[0]), "v"(p8[1]), "v"(l_run));
+    else asm volatile("" ::"v"(pb16), "v"(l_run));
   };
 
   // O^T += V^T P^T with the V tile in stage st.  Transposing read t gives this lane, for d row
@@ -334,6 +342,12 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2
   //   Split: op t: two MFMAs, keys 0-3 and 4-7 of the 8, each with its 4 V bytes twice (against
   //   16 hi and lo of P).
   auto pv = [&](int st) __attribute__((always_inline)) {
+    if (o_rescale) {
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) oacc[t] *= o_scale;
+      o_scale = 1.f;
+      o_rescale = false;
+    }
     const uint8_t* vp = lds + (st * kStage + kTile + v_lane);
     constexpr int NOPS = kNT;
     uint64_t buf[3];
@@ -360,20 +374,40 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2
   };
 
   // ---- main loop -------------------------------------------------------------------------------
-  // Tile x lives in stage (x - kt0) mod 4.  At the end of iteration t every wave has computed tile
-  // t, so in iteration t + 1 the stage of tile t takes tile t + 4.
+  // Tile x lives in stage (x - kt0) mod 4.  The two waves of a SIMD (wave w and w + 4) run half a
+  // tile apart, so that one's softmax overlaps the other's MFMAs.  Between barriers t - 1 and t:
+  //   group A (waves 0-3): PV(t), QK(t + 1) | softmax(t + 1)
+  //   group B (waves 4-7): softmax(t)       | PV(t), QK(t + 1)
+  // Both read tiles t and t + 1 there, so after barrier t - 1 the stage of tile t - 1 is free and
+  // takes tile t + 3, which has until barrier t + 1 to land.  Each group issues its share of those
+  // loads at the start of its softmax half, while its partner wave runs MFMAs (issued at the start
+  // of the MFMA half instead, they cost 11% with split Q).  The O rescale of a moved lazy max is
+  // applied at the next PV, so O is updated in one place (two places made the compiler spill O).
+  const bool group_a = wave < kNW / 2;
+  auto sees = [&](int t) __attribute__((always_inline)) { return t >= wt0 && t <= wt1; };
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();                     // tiles kt0 .. kt0 + 2 are in LDS
+  f32x4_t sacc[2];
+  if (sees(kt0)) {
+    qk(0, sacc);
+    if (group_a) softmax(kt0, sacc);
+  }
   for (int t = kt0; t <= kt1; ++t) {
-    const int st = (t - kt0) & (kNS - 1);
-    if (t >= wt0 && t <= wt1) {        // a tile none of this wave's rows sees adds nothing
-      f32x4_t sacc[2];
-      qk(st, sacc);
-      softmax(t, sacc);
-      pv(st);
+    const int st = (t - kt0) & (kNS - 1), st1 = (st + 1) & (kNS - 1);
+    const bool next = t + 1 <= kt1 && sees(t + 1);
+    if (!group_a) {
+      issue((st + 3) & (kNS - 1), min(t + 3, kt1), t + 3 > kt1);
+      if (sees(t)) softmax(t, sacc);
     }
-    issue((st + 3) & (kNS - 1), min(t + 3, kt1), t + 3 > kt1);   // into the stage of tile t - 1
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kMaxI));   // tile t + 1 has landed (this wave's part)
+    if (sees(t)) pv(st);
+    if (next) qk(st1, sacc);
+    asm volatile("" ::"v"(sacc[0]), "v"(sacc[1]));   // S stays in this half (not sunk past the barrier)
+    if (group_a) {
+      issue((st + 3) & (kNS - 1), min(t + 3, kt1), t + 3 > kt1);
+      if (next) softmax(t + 1, sacc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMaxI));   // tile t + 2 has landed (this wave's part)
     __syncthreads();                   // ... every wave's part, and every wave is done with tile t
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // nothing may land after the block ends

@@ -71,8 +71,8 @@ int cu_count() {
 // Supported (q dtype, head dim) pairs: native FP8 at head dim 256 (vLLM PR #63139, Overview) and
 // BF16 Q at head dim 512 (vLLM PR #60372, Overview), plus head dims 64, 96, 128 and 192 for both
 // (vLLM PR #63139, Overview: the FA4 native FP8 forward also covers 64/96/128/192), and 256 for
-// BF16 Q (same kernel).  96 is not a multiple of the 64-byte k-step: decode runs it in a 128
-// layout, FP8 prefill on the decode kernel.
+// BF16 Q (same kernel).  96 is not a multiple of the 64-byte k-step: decode and FP8 prefill run
+// it in a 128 layout whose last 32 bytes are zeros.
 bool supported_combo(int32_t q_dtype, int32_t d) {
   const bool small = d == 64 || d == 96 || d == 128 || d == 192;
   if (q_dtype == FP8ATTN_E4M3 || q_dtype == FP8ATTN_BF16_TO_E4M3) return small || d == 256;
@@ -508,15 +508,14 @@ fp8attn_status fp8attn_prefill_varlen(const fp8attn_attn_args* args, hipStream_t
   if (args->total_q == 0 || args->batch == 0) return ok();
   fp8attn::AttnParams p = make_params(args);
   hipError_t e;
-  if ((args->q_dtype == FP8ATTN_E4M3 || args->q_dtype == FP8ATTN_BF16_TO_E4M3) && args->head_dim != 96) {
+  if (args->q_dtype == FP8ATTN_E4M3 || args->q_dtype == FP8ATTN_BF16_TO_E4M3) {
     e = fp8attn::launch_prefill_fp8(p, args->head_dim, args->q_dtype == FP8ATTN_BF16_TO_E4M3, stream);
   } else if (args->head_dim == 512) {
     // the full-attention layers' head dim with bf16 Q: the d512 MFMA prefill
     e = fp8attn::launch_prefill_wide(p, args->q_dtype == FP8ATTN_BF16_SPLIT, stream);
   } else {
-    // BF16 queries, and head dim 96 (whose rows do not split into the prefill tiles' 64-byte
-    // k-steps): the split-KV kernel over 32-row query tiles (16 when no sequence has more rows
-    // per kv head), one split per tile.
+    // BF16 queries at head dims up to 256: the split-KV kernel over 32-row query tiles (16 when
+    // no sequence has more rows per kv head), one split per tile.
     const int G = args->num_q_heads / args->num_kv_heads;
     const int64_t rows = (int64_t)args->max_seqlen_q * G;
     p.tile_rows = rows > 16 && args->head_dim <= 256 ? 32 : 16;

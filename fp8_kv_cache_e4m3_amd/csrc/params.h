@@ -79,8 +79,8 @@ hipError_t launch_quantize_q(const void* q, int64_t ntok, int32_t nheads, int32_
 hipError_t launch_decode(const AttnParams& p, int q_mode, int head_dim, int64_t grid,
                          hipStream_t stream);
 
-// Native-FP8 prefill: 256 query rows per block, 64-key tiles through LDS.  head_dim 64, 128, 192
-// or 256 (96 runs on the decode kernel).
+// Native-FP8 prefill: 256 query rows per block, 64-key tiles through LDS.  head_dim 64, 96 (in a
+// 128-byte LDS row layout), 128, 192 or 256.
 // q_bf16: Q comes in bf16 and is quantized on load (q mode kQBf16E4M3), else E4M3 codes.
 hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, bool q_bf16, hipStream_t stream);
 

@@ -10,7 +10,7 @@
 //    group) pairs, token-major, so one K/V tile serves every q head of the group.  Each wave
 //    owns 32 rows.
 //  * K and V arrive one 64-token page at a time straight from HBM into LDS
-//    (global_load_lds_dwordx4) in a ring of three stages.  Key rows are padded to D + 16 bytes
+//    (global_load_lds_dwordx4) in a ring of four stages.  Key rows are padded to D + 16 bytes
 //    so that the MFMA operand reads below are free of bank conflicts.
 //  * The 8 waves form two groups half a tile apart, one barrier per tile: while one wave of a
 //    SIMD runs the softmax of a tile on the VALU, its partner runs MFMAs (PV of the previous tile
@@ -45,20 +45,22 @@ struct PrefillShape {
   static constexpr int RW = 32;           // rows per wave
   static constexpr int BM = NW * RW;      // rows per block
   static constexpr int BK = 64;           // keys per tile (one kernel page)
-  static constexpr int NCH = D / 16;      // 16-byte chunks per key row
-  static constexpr int KSTEP = D / 64;    // QK^T k-steps (64 d each)
+  // LDS row width: D, or 128 at D = 96 (the QK^T k-steps take 64 d; bytes 96-127 hold zeros)
+  static constexpr int DL = D == 96 ? 128 : D;
+  static constexpr int NCH = DL / 16;     // 16-byte chunks per LDS key row
+  static constexpr int KSTEP = DL / 64;   // QK^T k-steps (64 d each)
   static constexpr int NDT = D / 32;      // O^T tiles of 32 d-rows
-  static constexpr int RS = D + 16;       // LDS row stride: one 16-byte pad per key row
+  static constexpr int RS = DL + 16;      // LDS row stride: one 16-byte pad per key row
   static constexpr int SLOTS = NCH + 1;   // 16-byte LDS slots per key row
   static constexpr int TILE = BK * RS;    // bytes of one K (or V) tile in LDS
   static constexpr int LOADS = 2 * SLOTS; // wave-wide 1 KiB load instructions per K+V tile
   static constexpr int MAXI = (LOADS + NW - 1) / NW;  // load instructions per wave per tile
   static_assert(MAXI <= NDT + 2 * KSTEP, "loads are issued one per MFMA");
-  static_assert(D == 64 || D == 128 || D == 192 || D == 256, "head dim");
+  static_assert(D == 64 || D == 96 || D == 128 || D == 192 || D == 256, "head dim");
 };
 
-// Direct-to-LDS loads of one K and one V tile: D/16 + 1 16-byte slots per key row (the pad slot
-// gets a copy of the row's first chunk), 64 lanes per instruction, 2 * (D/16 + 1) instructions
+// Direct-to-LDS loads of one K and one V tile: DL/16 + 1 16-byte slots per key row (the pad slot
+// gets a copy of the row's first chunk), 64 lanes per instruction, 2 * (DL/16 + 1) instructions
 // per tile.  Wave w issues instructions w, w + 8, ...; every wave issues MAXI of them, a wave
 // that has one fewer repeating its previous one (the same bytes to the same place), so that the
 // issue is branch-free and every wave has the same number of loads in flight.
@@ -221,7 +223,7 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
 #pragma unroll
     for (int c = 0; c < S::KSTEP; ++c) {
       u32x4_t a = {0, 0, 0, 0}, bb = {0, 0, 0, 0};
-      if (rvalid) {
+      if (rvalid && 64 * c + 32 * lg < D) {   // (d past the head dim, at D = 96: zeros)
         a = *reinterpret_cast<const u32x4_t*>(qp + 64 * c);
         bb = *reinterpret_cast<const u32x4_t*>(qp + 64 * c + 16);
       }
@@ -254,8 +256,8 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
 
   // ---- tile loader: HBM -> LDS directly (global_load_lds_dwordx4, 16 bytes per lane) ---------
   // A wave-wide instruction fills 64 consecutive 16-byte LDS slots (lane i -> slot i).  Key rows
-  // occupy D/16 + 1 slots: D bytes of data and one pad slot, which receives a duplicate of the
-  // row's first chunk.  The pad makes the row stride D + 16 bytes (see the operand reads).
+  // occupy DL/16 + 1 slots: DL bytes of data and one pad slot, which receives a duplicate of the
+  // row's first chunk.  The pad makes the row stride DL + 16 bytes (see the operand reads).
   // Wave w issues instructions w, w + 8, ...; each lane's byte offset inside the 64-key tile is
   // fixed, so it is computed once and every load is a scalar tile base plus that offset.
   uint32_t loff[S::MAXI];
@@ -264,7 +266,10 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
     const int ins = load_instruction<D>(wave, t);
     const int sl = (ins % S::SLOTS) * 64 + lane;
     const int row = sl / S::SLOTS, posn = sl % S::SLOTS;
-    loff[t] = (uint32_t)(row * sT) + 16u * (uint32_t)(posn == S::NCH ? 0 : posn);
+    // chunks past the head dim (D = 96) take an offset outside every buffer's range: zeros
+    loff[t] = 16 * posn >= D && posn != S::NCH
+                  ? 0xFFFFFFF0u
+                  : (uint32_t)(row * sT) + 16u * (uint32_t)(posn == S::NCH ? 0 : posn);
   }
   auto page_id = [&](int kt) __attribute__((always_inline)) -> int {
     return bt[ps == S::BK ? kt : (kt * S::BK) / ps];
@@ -424,7 +429,8 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
 #pragma unroll
     for (int c = 0; c < S::KSTEP; ++c) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) qw[c][k] = *reinterpret_cast<const u32x4_t*>(qp + 64 * c + 8 * k);
+      for (int k = 0; k < 4; ++k)
+        qw[c][k] = 64 * c + 32 * lg < D ? *reinterpret_cast<const u32x4_t*>(qp + 64 * c + 8 * k) : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
     for (int c = 0; c < S::KSTEP; ++c) {
@@ -434,7 +440,7 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
       qop[c] = i32x8_t{(int)e[0][0], (int)e[0][1], (int)e[1][0], (int)e[1][1],
                        (int)e[2][0], (int)e[2][1], (int)e[3][0], (int)e[3][1]};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) qop[c][k] = rvalid ? qop[c][k] : 0;
+      for (int k = 0; k < 8; ++k) qop[c][k] = rvalid && 64 * c + 32 * lg < D ? qop[c][k] : 0;
     }
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -554,6 +560,9 @@ hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, bool q_bf16, hi
   } else if (head_dim == 192) {
     if (q_bf16) launch_prefill_pair<192, true>(p, grid, nqb, grid_split, nqb_split, stream);
     else launch_prefill_pair<192, false>(p, grid, nqb, grid_split, nqb_split, stream);
+  } else if (head_dim == 96) {
+    if (q_bf16) launch_prefill_pair<96, true>(p, grid, nqb, grid_split, nqb_split, stream);
+    else launch_prefill_pair<96, false>(p, grid, nqb, grid_split, nqb_split, stream);
   } else if (head_dim == 128) {
     if (q_bf16) launch_prefill_pair<128, true>(p, grid, nqb, grid_split, nqb_split, stream);
     else launch_prefill_pair<128, false>(p, grid, nqb, grid_split, nqb_split, stream);

@@ -2,8 +2,8 @@
 fp64 CPU oracle (every row compared unless stated):
 
 * the single-P FP8 prefill instance (a q block whose first row sees at least 512 keys): the
-  sliding-window prefill at reduced size that keeps its 1024-key window, and head dims 64, 128,
-  192 and 256 with no window; each with E4M3 codes and with bf16 Q quantized in the kernel, the
+  sliding-window prefill at reduced size that keeps its 1024-key window, and head dims 64, 96,
+  128, 192 and 256 with no window (96 also with a 700-key window); each with E4M3 codes and with bf16 Q quantized in the kernel, the
   two bit for bit equal;
 * FP8 prefill over 128-token framework blocks;
 * GQA groups that do not divide the 16-row decode tile or the 256-row prefill block (3 and 6);
@@ -44,6 +44,8 @@ SINGLE_P_CASES = {
     # 4 q / 2 kv heads, d256, W1024 (most q blocks see 1024 keys)
     "swa_prefill_window_kept": lambda: wl.custom("e4m3", 256, 4, 2, 1024, [2048, 2048], [2048, 2048], seed=41),
     "d64_no_window": lambda: wl.custom("e4m3", 64, 4, 2, -1, [1500, 700], [1500, 300], seed=42),
+    "d96_no_window": lambda: wl.custom("e4m3", 96, 4, 2, -1, [1500, 700], [1500, 300], seed=47),
+    "d96_window_700_gqa4": lambda: wl.custom("e4m3", 96, 8, 2, 700, [1600, 333], [1600, 333], seed=48),
     "d128_no_window": lambda: wl.custom("e4m3", 128, 4, 2, -1, [1500, 700], [1500, 300], seed=43),
     "d192_no_window": lambda: wl.custom("e4m3", 192, 4, 2, -1, [1500, 700], [1500, 300], seed=44),
     "d256_no_window": lambda: wl.custom("e4m3", 256, 4, 2, -1, [1500, 700], [1500, 300], seed=45),
@@ -159,6 +161,7 @@ def test_per_sequence_head_descales_all_kernels(q_dtype, d, entry, splits, fused
     ("e4m3", 128, 4, 2, 100, [1333, 650], [1333, 9], "prefill", 0, False, 64),   # split-P only
     ("e4m3", 256, 4, 2, -1, [1333, 650], [1333, 9], "prefill", 0, False, 128),
     ("bf16", 128, 4, 2, -1, [333, 650], [333, 9], "prefill", 0, False, 64),
+    ("e4m3", 96, 4, 2, -1, [1333, 650], [1333, 9], "prefill", 0, True, 128),     # d96 in the 128 layout
 ])
 def test_nan_codes_past_sequence_end(q_dtype, d, hq, hkv, window, seqlens, qlens, entry, splits, fused, page):
     w = wl.custom(q_dtype, d, hq, hkv, window, seqlens, qlens, seed=81)

@@ -415,6 +415,106 @@ def load_traffic(kernel_key):
     return ent.get("hbm_bytes_per_launch")
 
 
+def decode_timeline(launches=5):
+    """Phase stamps of the split-grid decode kernel on the sliding-window decode workload, from the
+    timeline build of the library (python fp8_kv_cache_e4m3_amd/build.py --timeline): per block,
+    its start, the first K/V unit computed by each wave, the end of each wave's stream, the merge
+    and the output stores, in shader-clock ticks converted with the blocks' real-time clock
+    (100 MHz).  Prints the distributions over the blocks of each measured launch as one JSON line."""
+    import ctypes
+    import numpy as np
+    import torch
+    import fp8_kv_cache_e4m3_amd as fa
+    import workloads as wl
+
+    path = os.path.join(os.path.dirname(fa.LIB_PATH), "libfp8attn_timeline.so")
+    if not os.path.exists(path):
+        sys.exit(f"{path} is missing: build it with python fp8_kv_cache_e4m3_amd/build.py --timeline")
+    tl = ctypes.CDLL(path)
+    tl.fp8attn_decode_paged.argtypes = fa.LIB.fp8attn_decode_paged.argtypes
+    tl.fp8attn_decode_paged.restype = ctypes.c_int32
+    tl.fp8attn_decode_timeline.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+    tl.fp8attn_decode_timeline.restype = ctypes.c_int
+    tl.fp8attn_decode_timeline_clear.restype = ctypes.c_int
+    nblk, nslot = 4096, 16
+    runners = [Runner(wl.swa_decode(device="cuda", seed=100 + s), "decode") for s in range(4)]
+    w = runners[0].w
+    assert runners[0].ws is None and runners[0].splits == 1
+    grid = w.num_kv_heads * w.batch
+    assert grid <= nblk
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def launch(r):
+        st = tl.fp8attn_decode_paged(ctypes.byref(r.args), 0, None, 0, None, None, sh)
+        assert st == 0
+
+    for i in range(20):
+        launch(runners[i % 4])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(40):
+        launch(runners[i % 4])
+    b.record()
+    torch.cuda.synchronize()
+    ms_avg = a.elapsed_time(b) / 40
+    buf = np.zeros(nblk * nslot, dtype=np.uint64)
+
+    def q(x):
+        return {k: round(float(np.percentile(x, p)), 2) for k, p in (("min", 0), ("p10", 10), ("p50", 50),
+                                                                      ("p90", 90), ("max", 100))}
+    res = []
+    for i in range(launches):
+        assert tl.fp8attn_decode_timeline_clear() == 0
+        r = runners[i % 4]
+        a.record()
+        launch(r)
+        b.record()
+        torch.cuda.synchronize()
+        assert tl.fp8attn_decode_timeline(buf.ctypes.data, buf.size) == 0
+        t = buf.reshape(nblk, nslot)[:grid].astype(np.int64)
+        assert (t[:, 0] > 0).all() and (t[:, 10] > 0).all(), "a block left no stamps"
+        # s_memtime counts the shader clock of each XCD and is not aligned across XCDs; the 100 MHz
+        # real-time clock is.  Absolute times: the block's real-time start plus its own shader-clock
+        # offsets, converted with the ratio of the two clocks over the block.
+        rt = (t[:, 14] - t[:, 13]).astype(np.float64) / 100.0            # us
+        mt = (t[:, 10] - t[:, 0]).astype(np.float64)
+        ok = rt > 0
+        tick_per_us = float(np.median(mt[ok] / rt[ok]))
+        start = (t[:, 13] - t[:, 13].min()) / 100.0
+        at = start[:, None] + (t[:, :11] - t[:, :1]) / tick_per_us       # [blocks, 11] us
+        first = at[:, 1:5].max(1)
+        stream_end = at[:, 5:9].max(1)
+        end = at[:, 10]
+        xcc = (t[:, 12] & 0xF)
+        span = float(end.max())
+        # blocks streaming over time (between their first unit and the end of their stream)
+        grid_us = np.arange(0.0, span, 0.5)
+        active = ((first[None, :] <= grid_us[:, None]) & (stream_end[None, :] > grid_us[:, None])).sum(1)
+        full = grid_us[active >= 0.9 * grid]
+        res.append({
+            "launch_ms_events": round(a.elapsed_time(b), 4),
+            "span_us": round(span, 2),
+            "shader_ticks_per_us": round(tick_per_us, 1),
+            "block_start_us": q(start),
+            "first_unit_done_us": q(first),
+            "stream_end_us": q(stream_end),
+            "block_end_us": q(end),
+            "first_unit_after_start_us": q(first - start),
+            "stream_us": q(stream_end - first),
+            "wave_stream_end_spread_us": q(at[:, 5:9].max(1) - at[:, 5:9].min(1)),
+            "merge_us": q(at[:, 9] - stream_end),
+            "store_us": q(at[:, 10] - at[:, 9]),
+            "ninety_pct_streaming_us": [round(float(full.min()), 1), round(float(full.max()), 1)] if len(full) else None,
+            "blocks": int(grid),
+            "blocks_per_xcc": {int(x): int((xcc == x).sum()) for x in np.unique(xcc)},
+            "end_p50_by_xcc_us": {int(x): round(float(np.median(end[xcc == x])), 2) for x in np.unique(xcc)},
+        })
+    print(json.dumps({"workload": "sliding-window decode (B32, L U[1024, 8192], 32/16 heads, d256, W1024)",
+                      "kernel": "decode_kernel (timeline build)", "avg_launch_ms_events": round(ms_avg, 4),
+                      "launches": res}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -431,6 +531,8 @@ def main():
     ap.add_argument("--separate-quantize", action="store_true",
                     help="quantize Q with its own call before attention (two launches per step) instead of "
                          "inside the attention kernel")
+    ap.add_argument("--timeline", action="store_true",
+                    help="phase stamps of the decode kernel per block (needs the timeline build of the library)")
     args = ap.parse_args()
     fused = not args.separate_quantize
     if args.gpus != 1:
@@ -443,6 +545,9 @@ def main():
     import fp8_kv_cache_e4m3_amd  # noqa: F401  (fails loudly if the HIP library is missing)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.timeline:
+        decode_timeline()
+        return
     nsets = 4
 
     makers = {

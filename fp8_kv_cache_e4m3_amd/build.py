@@ -1,9 +1,11 @@
 """Build libfp8attn.so in-tree with hipcc for gfx950.
 
-    python fp8_kv_cache_e4m3_amd/build.py        # runs without importing (and loading) the package
+    python fp8_kv_cache_e4m3_amd/build.py             # runs without importing (and loading) the package
+    python fp8_kv_cache_e4m3_amd/build.py --timeline  # libfp8attn_timeline.so: the same library with the
+                                                      # decode kernel's phase stamps (bench.py --timeline)
 
 Every source is compiled on each call (no stale objects); objects go to ``_build/``
-next to this file and the shared library lands in this package directory.
+(``_build_timeline/``) next to this file and the shared library lands in this package directory.
 """
 from __future__ import annotations
 
@@ -17,6 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8attn.so")
+TIMELINE_LIB = os.path.join(PKG, "libfp8attn_timeline.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CLANGXX = "/opt/rocm/lib/llvm/bin/clang++"
 
@@ -38,12 +41,12 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-
           "-I" + os.path.join(os.path.dirname(PKG), "include")]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
     extra = os.environ.get("EXTRA_HIPCC_FLAGS", "").split()   # e.g. -D tuning switches for experiments
-    cmd = [HIPCC] + COMMON + extra + lang + ["-c", path, "-o", obj]
+    cmd = [HIPCC] + COMMON + list(defines) + extra + lang + ["-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -54,14 +57,17 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, timeline: bool = False) -> str:
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(BUILD, exist_ok=True)
+    build_dir = BUILD + "_timeline" if timeline else BUILD
+    lib = TIMELINE_LIB if timeline else LIB
+    defines = ["-DFP8ATTN_TIMELINE"] if timeline else []
+    os.makedirs(build_dir, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, defines), srcs))
+    tmp = lib + ".tmp"
     # One HIP runtime per process: torch ships its own libamdhip64.so without a SONAME and its
     # libraries load it by the unversioned name.  Linking against that file records the same
     # unversioned name here, so in a process that already imported torch the loader reuses
@@ -81,11 +87,11 @@ def build(verbose: bool = True) -> str:
     missing = [l.split()[-1] for l in r.stdout.splitlines() if "__device_stub__" in l]
     if missing:
         raise RuntimeError("kernel host stubs are undefined in the linked library: " + ", ".join(missing))
-    shutil.move(tmp, LIB)
+    shutil.move(tmp, lib)
     if verbose:
-        print(f"[build] {LIB}")
-    return LIB
+        print(f"[build] {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build()
+    build(timeline="--timeline" in sys.argv[1:])

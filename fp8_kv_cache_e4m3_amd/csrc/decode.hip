@@ -36,6 +36,21 @@
 
 namespace fp8attn {
 
+// Timeline builds only (build.py --timeline, for bench.py --timeline): the split-grid decode kernel
+// stamps the phases of each of its first kTimelineBlocks blocks with the shader clock
+// (s_memtime), one 64-bit slot per stamp, written by lane 0 of the stamping wave:
+//   0 entry, 1-4 first unit computed (waves 0-3), 5-8 stream done (waves 0-3), 9 merge done,
+//   10 outputs stored, 11 HW_ID, 12 XCC_ID, 13/14 real-time clock at entry / end.
+constexpr int kTimelineBlocks = 4096;
+constexpr int kTimelineSlots = 16;
+#ifdef FP8ATTN_TIMELINE
+__device__ uint64_t g_decode_timeline[kTimelineBlocks * kTimelineSlots];
+__device__ __forceinline__ void tl_mark(int slot, uint64_t v) {
+  if ((threadIdx.x & 63) == 0 && blockIdx.x < kTimelineBlocks)
+    g_decode_timeline[blockIdx.x * kTimelineSlots + slot] = v;
+}
+#endif
+
 constexpr float kLazyMax = 8.0f;   // log2 units: the running max moves by more than 2^8 or not at all
 
 template <int D>
@@ -169,6 +184,14 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int G = p.group;
+#ifdef FP8ATTN_TIMELINE
+  if (!BAL && wave == 0) {
+    tl_mark(0, __builtin_amdgcn_s_memtime());
+    tl_mark(11, (uint64_t)__builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 4));
+    tl_mark(12, (uint64_t)__builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 20));
+    tl_mark(13, __builtin_amdgcn_s_memrealtime());
+  }
+#endif
 
   // Every per-item scalar of the prologue is requested here, before any branch, so that the
   // loads share one round trip.  A NULL descale reads a valid stand-in address (the sequence's
@@ -468,10 +491,16 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
       for (int k = 0; k < NBUF; ++k) {
         const int uk = u + 4 * k;
         if (uk < su1) compute(buf[k], uk);
+#ifdef FP8ATTN_TIMELINE
+        if (!BAL && k == 0 && u == u0) tl_mark(1 + wave, __builtin_amdgcn_s_memtime());
+#endif
         issue(buf[k], uk + 4 * NBUF);
       }
     }
   }
+#ifdef FP8ATTN_TIMELINE
+  if (!BAL) tl_mark(5 + wave, __builtin_amdgcn_s_memtime());
+#endif
   l_run = sum_over_groups(l_run);
 
   // ---- merge the 4 waves through LDS --------------------------------------------------------
@@ -498,6 +527,9 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
     }
   }
   __syncthreads();
+#ifdef FP8ATTN_TIMELINE
+  if (!BAL && wave == 0) tl_mark(9, __builtin_amdgcn_s_memtime());
+#endif
 
   // ---- final: thread -> (row, d-part) -------------------------------------------------------
   {
@@ -546,6 +578,12 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
       }
     }
   }
+#ifdef FP8ATTN_TIMELINE
+  if (!BAL && wave == 0) {
+    tl_mark(10, __builtin_amdgcn_s_memtime());
+    tl_mark(14, __builtin_amdgcn_s_memrealtime());
+  }
+#endif
   // a block of the balanced partition runs several tiles in turn: the next tile's merge must not
   // overwrite the LDS this one is still reading
   if constexpr (BAL) __syncthreads();
@@ -1149,5 +1187,23 @@ hipError_t launch_decode(const AttnParams& p, int q_mode, int head_dim, int64_t 
   else launch_decode_modes<false>(p, q_mode, head_dim, g, stream);
   return hipGetLastError();
 }
+
+#ifdef FP8ATTN_TIMELINE
+// Copies the stamps of the last split-grid decode launch (kTimelineBlocks x kTimelineSlots
+// uint64 values, blocks past the grid left as they were) to host memory; 0 on success.
+extern "C" __attribute__((visibility("default"))) int fp8attn_decode_timeline(uint64_t* host_dst, int64_t max_values) {
+  const int64_t n = (int64_t)kTimelineBlocks * kTimelineSlots;
+  if (host_dst == nullptr || max_values < n) return -1;
+  if (hipDeviceSynchronize() != hipSuccess) return -2;
+  return hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(g_decode_timeline), n * sizeof(uint64_t), 0,
+                             hipMemcpyDeviceToHost) == hipSuccess ? 0 : -3;
+}
+// Clears the stamps (zeros).
+extern "C" __attribute__((visibility("default"))) int fp8attn_decode_timeline_clear(void) {
+  static uint64_t zeros[kTimelineBlocks * kTimelineSlots];
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_decode_timeline), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice) ==
+                 hipSuccess ? 0 : -1;
+}
+#endif
 
 }  // namespace fp8attn

@@ -42,6 +42,8 @@ KERNEL_SOURCES = {
                "fp8_kv_cache_e4m3_amd/csrc/params.h"],
     "prefill": ["fp8_kv_cache_e4m3_amd/csrc/prefill.hip", "fp8_kv_cache_e4m3_amd/csrc/device.h",
                 "fp8_kv_cache_e4m3_amd/csrc/params.h"],
+    "prefill_wide": ["fp8_kv_cache_e4m3_amd/csrc/prefill_wide.hip", "fp8_kv_cache_e4m3_amd/csrc/device.h",
+                     "fp8_kv_cache_e4m3_amd/csrc/params.h"],
     "combine": ["fp8_kv_cache_e4m3_amd/csrc/combine.hip", "fp8_kv_cache_e4m3_amd/csrc/device.h",
                 "fp8_kv_cache_e4m3_amd/csrc/params.h"],
 }
@@ -597,7 +599,7 @@ def main():
             # the same bf16-Q workloads with QK^T on the FP8 MFMA (split Q)
             ("full_decode_split_q", lambda s: wl.full_decode(device="cuda", seed=200 + s), "decode", 4, "hbm", True),
             ("spec_verify_split_q", lambda s: wl.spec_verify(device="cuda", seed=300 + s), "decode", 2, "hbm", True),
-            # d512 prefill (BF16 Q and split Q): the decode kernel over 16-row tiles, no MFMA prefill kernel
+            # d512 prefill (BF16 Q and split Q): the wide MFMA prefill kernel
             ("full_prefill", lambda s: wl.full_prefill(device="cuda", seed=500 + s), "prefill", 2, "mfma", False),
             ("full_prefill_split_q", lambda s: wl.full_prefill(device="cuda", seed=500 + s), "prefill", 2, "mfma",
              True),
@@ -616,7 +618,8 @@ def main():
                 e["step"] = "quantize_q, then the attention call on E4M3 codes (attention_ms: that call alone)"
             # HBM bytes of the step's kernels (decode plus the partition's combine; both prefill instances)
             keys = {"full_decode": ["decode_full", "decode_full_combine"], "spec_verify": ["decode_spec"],
-                    "swa_prefill": ["prefill_swa", "prefill_swa_splitp"]}.get(name)
+                    "swa_prefill": ["prefill_swa", "prefill_swa_splitp"], "full_prefill": ["prefill_full"],
+                    "full_prefill_split_q": ["prefill_full_split_q"]}.get(name)
             tr = [load_traffic(k) for k in keys] if keys else [None]
             e["traffic"] = sum(tr) if fz and all(t is not None for t in tr) else None
             mfma_peak = FP8_PEAK_TFLOPS if ww.q_dtype == "e4m3" or split else BF16_PEAK_TFLOPS

@@ -41,9 +41,9 @@ namespace fp8attn {
 // (s_memtime), one 64-bit slot per stamp, written by lane 0 of the stamping wave:
 //   0 entry, 1-4 first unit computed (waves 0-3), 5-8 stream done (waves 0-3), 9 merge done,
 //   10 outputs stored, 11 HW_ID, 12 XCC_ID, 13/14 real-time clock at entry / end.
+#ifdef FP8ATTN_TIMELINE
 constexpr int kTimelineBlocks = 4096;
 constexpr int kTimelineSlots = 16;
-#ifdef FP8ATTN_TIMELINE
 __device__ uint64_t g_decode_timeline[kTimelineBlocks * kTimelineSlots];
 __device__ __forceinline__ void tl_mark(int slot, uint64_t v) {
   if ((threadIdx.x & 63) == 0 && blockIdx.x < kTimelineBlocks)
@@ -180,6 +180,10 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
   __shared__ __attribute__((aligned(16))) float sm_o[4][16][S::RS];
   __shared__ float sm_m[4][16];
   __shared__ float sm_l[4][16];
+  // The balanced partition at head dim 512 keeps the Q^T operands in LDS (the 4 waves hold the
+  // same rows): in registers they pushed the loop past the 512 registers of a wave (spills).
+  constexpr bool QLDS = DP == 512 && BAL;
+  __shared__ __attribute__((aligned(16))) uint8_t sm_q[QLDS ? 16384 : 16];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
@@ -354,16 +358,25 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
   // S^T tile of a unit: rows = its 16 keys, columns = the 16 query rows
   auto qk = [&](const u32x4_t (&kk)[S::KCH]) __attribute__((always_inline)) -> f32x4_t {
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+    int qoff = lane;
+    if constexpr (QLDS) asm volatile("" : "+v"(qoff));   // (read Q from LDS for every unit)
     if constexpr (SPLIT) {   // the split accumulation: K hi + (K lo) / 16
       f32x4_t slo = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < S::KCH; ++c) {
         const uint64_t k0 = (uint64_t)kk[c][0] | ((uint64_t)kk[c][1] << 32);
         const uint64_t k1 = (uint64_t)kk[c][2] | ((uint64_t)kk[c][3] << 32);
-        sacc = mfma_fp8_16x16x32(k0, qr.q[2 * c], sacc);
-        slo = mfma_fp8_16x16x32(k0, qlo[2 * c], slo);
-        sacc = mfma_fp8_16x16x32(k1, qr.q[2 * c + 1], sacc);
-        slo = mfma_fp8_16x16x32(k1, qlo[2 * c + 1], slo);
+        uint64_t h0 = qr.q[2 * c], h1 = qr.q[2 * c + 1], l0 = qlo[2 * c], l1 = qlo[2 * c + 1];
+        if constexpr (QLDS) {
+          h0 = *reinterpret_cast<const uint64_t*>(sm_q + ((2 * c) * 64 + qoff) * 8);
+          h1 = *reinterpret_cast<const uint64_t*>(sm_q + ((2 * c + 1) * 64 + qoff) * 8);
+          l0 = *reinterpret_cast<const uint64_t*>(sm_q + 8192 + ((2 * c) * 64 + qoff) * 8);
+          l1 = *reinterpret_cast<const uint64_t*>(sm_q + 8192 + ((2 * c + 1) * 64 + qoff) * 8);
+        }
+        sacc = mfma_fp8_16x16x32(k0, h0, sacc);
+        slo = mfma_fp8_16x16x32(k0, l0, slo);
+        sacc = mfma_fp8_16x16x32(k1, h1, sacc);
+        slo = mfma_fp8_16x16x32(k1, l1, slo);
       }
       return sacc + slo * 0.0625f;
     }
@@ -375,8 +388,13 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
         sacc = mfma_fp8_16x16x32(k0, qr.q[2 * c], sacc);
         sacc = mfma_fp8_16x16x32(k1, qr.q[2 * c + 1], sacc);
       } else {
-        sacc = mfma_bf16_16x16x32(e4m3x8_to_bf16(kk[c][0], kk[c][1]), qr.q[2 * c], sacc);
-        sacc = mfma_bf16_16x16x32(e4m3x8_to_bf16(kk[c][2], kk[c][3]), qr.q[2 * c + 1], sacc);
+        bf16x8_t q0 = qr.q[2 * c], q1 = qr.q[2 * c + 1];
+        if constexpr (QLDS) {
+          q0 = *reinterpret_cast<const bf16x8_t*>(sm_q + ((2 * c) * 64 + qoff) * 16);
+          q1 = *reinterpret_cast<const bf16x8_t*>(sm_q + ((2 * c + 1) * 64 + qoff) * 16);
+        }
+        sacc = mfma_bf16_16x16x32(e4m3x8_to_bf16(kk[c][0], kk[c][1]), q0, sacc);
+        sacc = mfma_bf16_16x16x32(e4m3x8_to_bf16(kk[c][2], kk[c][3]), q1, sacc);
       }
     }
     return sacc;
@@ -477,6 +495,22 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
     UnitRegs<DP> buf[NBUF];
 #pragma unroll
     for (int k = 0; k < NBUF; ++k) issue(buf[k], u0 + 4 * k);
+    if constexpr (QLDS) {
+      // wave 0 writes the Q^T operand image (the same in every wave); the previous tile of this
+      // block finished reading its image before the barrier that ended that tile
+      if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < 2 * S::KCH; ++i) {
+          if constexpr (SPLIT) {
+            *reinterpret_cast<uint64_t*>(sm_q + (i * 64 + lane) * 8) = qr.q[i];
+            *reinterpret_cast<uint64_t*>(sm_q + 8192 + (i * 64 + lane) * 8) = qlo[i];
+          } else {
+            *reinterpret_cast<bf16x8_t*>(sm_q + (i * 64 + lane) * 16) = qr.q[i];
+          }
+        }
+      }
+      __syncthreads();
+    }
     if constexpr (QM == kQBf16E4M3) {
       // quantize bf16 Q with the arithmetic of the stand-alone quantize call (identical codes)
       const double rcp = 1.0 / (double)qd;

@@ -11,7 +11,9 @@ fp64 CPU oracle (every row compared unless stated):
 * pool slots past a sequence's length holding E4M3 NaN codes (never written for the sequence, never
   visible): outputs bit for bit unchanged;
 * the sliding-window prefill at full size on whole q blocks, in the launch configuration the bench
-  times (bf16 Q quantized in the kernel).
+  times (bf16 Q quantized in the kernel);
+* the d512 prefill kernel (bf16 and split Q) on 128-token blocks, with a window, and with GQA
+  groups that do not divide its 16-row waves.
 """
 import numpy as np
 import pytest
@@ -205,3 +207,23 @@ def test_swa_prefill_full_size_whole_blocks():
     toks = sorted(toks)
     o_ref, l_ref, _ = oracle_run(w, tokens=toks)
     compare(o1, o_ref, l1, l_ref, rows=toks, label=f"full-size sliding-window prefill rows={len(toks)}")
+
+
+# ------------------------------------------------------------------------------------------
+# the d512 prefill kernel beyond the full-attention workload: 128-token framework blocks (a tile
+# starting inside a block), a sliding window, GQA 6 (a token's rows straddle waves and blocks)
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("split", [False, True], ids=["bf16", "split"])
+@pytest.mark.parametrize("hq,hkv,window,seqlens,qlens,page", [
+    (16, 2, -1, [700, 1300, 90], [700, 333, 90], 128),
+    (8, 2, 300, [1500, 600], [1500, 600], 64),
+    (12, 2, -1, [400, 1000], [400, 257], 64),
+])
+def test_wide_prefill_cases(hq, hkv, window, seqlens, qlens, page, split):
+    w = wl.custom("bf16", 512, hq, hkv, window, seqlens, qlens, seed=61 + hq)
+    if page != 64:
+        w = with_page_size(w, page)
+    log(f"[case] d512 prefill G={hq // hkv} W={window} page={page} split={split}")
+    o_ref, l_ref, _ = oracle_run(w)
+    o, l, _, _ = gpu_run(w, "prefill", split_q=split)
+    compare(o, o_ref, l, l_ref, label=f"d512 prefill G={hq // hkv} W={window} page={page} split={split}")

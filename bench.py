@@ -46,6 +46,8 @@ KERNEL_SOURCES = {
                      "fp8_kv_cache_e4m3_amd/csrc/params.h"],
     "combine": ["fp8_kv_cache_e4m3_amd/csrc/combine.hip", "fp8_kv_cache_e4m3_amd/csrc/device.h",
                 "fp8_kv_cache_e4m3_amd/csrc/params.h"],
+    "verify": ["fp8_kv_cache_e4m3_amd/csrc/verify.hip", "fp8_kv_cache_e4m3_amd/csrc/device.h",
+               "fp8_kv_cache_e4m3_amd/csrc/params.h"],
 }
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -618,6 +620,7 @@ def main():
                 e["step"] = "quantize_q, then the attention call on E4M3 codes (attention_ms: that call alone)"
             # HBM bytes of the step's kernels (decode plus the partition's combine; both prefill instances)
             keys = {"full_decode": ["decode_full", "decode_full_combine"], "spec_verify": ["decode_spec"],
+                    "spec_verify_split_q": ["decode_spec_split_q"],
                     "swa_prefill": ["prefill_swa", "prefill_swa_splitp"], "full_prefill": ["prefill_full"],
                     "full_prefill_split_q": ["prefill_full_split_q"]}.get(name)
             tr = [load_traffic(k) for k in keys] if keys else [None]

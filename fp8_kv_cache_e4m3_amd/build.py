@@ -33,7 +33,7 @@ def _torch_lib_dir():
     return d if os.path.exists(os.path.join(d, "libamdhip64.so")) else None
 
 SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "combine.hip", "prefill.hip", "prefill_wide.hip",
-           "cache_write.hip"]
+           "verify.hip", "cache_write.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops (v_pk_*_f32).
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -219,8 +219,9 @@ struct DecodePlan {
 // sequence's tiles side by side.
 // The split grid takes 32-row tiles when a sequence has more than 16 rows per kv head and the head
 // dim is at most 256: each K/V unit is then loaded once for 32 rows instead of once per 16.  At
-// head dim 512 the two halves' O accumulators alone fill the 256 accumulation registers of a wave
-// and the kernel spilled in its loop (5x slower), so 512 keeps 16-row tiles.
+// head dim 512 the two halves' O accumulators alone fill the 256 accumulation registers of a
+// decode wave (the kernel spilled in its loop, 5x slower), so 512 keeps 16-row tiles there; with
+// split Q, 32-row tiles at 512 run in the verify kernel, whose waves split the head dim of O.
 constexpr int32_t kBalancedMinUnits = 256;   // 4096 keys
 constexpr int32_t kMaxParts = 1 << 20;
 
@@ -257,7 +258,7 @@ DecodePlan plan_decode(const fp8attn_attn_args* a, int32_t requested) {
     pl.grid = R;
     return pl;
   }
-  if (rows > 16 && a->head_dim <= 256) {
+  if (rows > 16 && (a->head_dim <= 256 || (a->head_dim == 512 && a->q_dtype == FP8ATTN_BF16_SPLIT))) {
     pl.tile_rows = 32;
     pl.row_groups = (int32_t)((rows + 31) / 32);
     items = (int64_t)a->num_kv_heads * a->batch * pl.row_groups;
@@ -316,7 +317,9 @@ fp8attn_status run_decode(const char* fn, const fp8attn_attn_args* args, const D
     p.part_o = reinterpret_cast<float*>(ws);
     p.part_lse = reinterpret_cast<float*>(ws + round_up((size_t)pl.splits * rows * args->head_dim * sizeof(float)));
   }
-  hipError_t e = fp8attn::launch_decode(p, args->q_dtype, args->head_dim, pl.grid, stream);
+  hipError_t e = pl.tile_rows == 32 && args->head_dim == 512
+                     ? fp8attn::launch_verify(p, pl.grid, stream)
+                     : fp8attn::launch_decode(p, args->q_dtype, args->head_dim, pl.grid, stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   if (pl.balanced) {
     e = fp8attn::launch_combine_parts(p.part_o, p.part_lse, p.seg_meta, args->cu_seqlens_q, args->batch,

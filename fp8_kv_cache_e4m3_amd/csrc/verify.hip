@@ -333,12 +333,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     }
   } else {
     // ================================ PV waves =================================================
-    const int v = wave - 4;                           // O^T columns 128 v .. 128 v + 127
+    const int v = wave - 4;                           // this wave's 128 head-dim columns: below
     const int n = lane & 31, g = lane >> 5;           // this lane's row (MFMA column), lane group
+    // O^T tile dt (0..3) of PV wave v: row m < 16 holds column cb + 16 dt + m and row m >= 16 column
+    // cb + 128 + 16 dt + m - 16, with cb = 256 (v / 2) + 64 (v % 2).  The two 16-lane halves of a
+    // transposing read then touch bytes 128 apart: with the 528-byte key rows, the read's 32 lanes
+    // cover 32 distinct 8-byte slots of a 256-byte window (no bank conflicts).
+    const int cb = 256 * (v >> 1) + 64 * (v & 1);
     // V^T transposing reads: this lane supplies key row 16 g + 8 o + (lane % 16) / 2 and 8-byte half
-    // lane % 2 at columns 32 dt + 16 ((lane / 16) % 2); lane (n, g) receives column 32 dt + n of
-    // keys 16 g + 8 o .. + 7
-    const int v_lane = lane_offset((16 * g + ((lane & 15) >> 1)) * kRS + 16 * ((lane >> 4) & 1) + 8 * (lane & 1));
+    // lane % 2 at column cb + 16 dt + 128 ((lane / 16) % 2); lane (n, g) receives O^T row n's column
+    // of keys 16 g + 8 o .. + 7
+    const int v_lane = lane_offset((16 * g + ((lane & 15) >> 1)) * kRS + 128 * ((lane >> 4) & 1) + 8 * (lane & 1));
 
     f32x16_t oacc[kDT];
 #pragma unroll
@@ -361,8 +366,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
         i32x8_t a[kDT];
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) {
-          const i32x2_t v0 = lds_read_tr8(vst + 32 * (kDT * v + dt));
-          const i32x2_t v1 = lds_read_tr8(vst + 8 * kRS + 32 * (kDT * v + dt));
+          const i32x2_t v0 = lds_read_tr8(vst + cb + 16 * dt);
+          const i32x2_t v1 = lds_read_tr8(vst + 8 * kRS + cb + 16 * dt);
           a[dt] = i32x8_t{v0[0], v0[1], v1[0], v1[1], v0[0], v0[1], v1[0], v1[1]};
         }
         const bool grow = m_t > m_ref + kSlack;
@@ -384,7 +389,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
       __syncthreads();
     }
 
-    // ---- epilogue: lane (n, g) holds, for O^T tile dt, columns 32 (4 v + dt) + 8 a + 4 g + 0..3 ----
+    // ---- epilogue: lane (n, g) holds, for O^T tile dt and a = 0..3, rows 8 a + 4 g + 0..3, i.e.
+    // columns cb + 16 dt + 8 a + 4 g + 0..3 (a < 2) and cb + 128 + 16 dt + 8 (a - 2) + 4 g + 0..3 ----
     const int r = row0 + n;
     if (r < nrows) {
       const int tk = r / G, hh = h * G + r % G;
@@ -399,7 +405,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
           for (int a4 = 0; a4 < 4; ++a4) {
             const bf16x4_t o = {(__bf16)(oacc[dt][4 * a4] * inv), (__bf16)(oacc[dt][4 * a4 + 1] * inv),
                                 (__bf16)(oacc[dt][4 * a4 + 2] * inv), (__bf16)(oacc[dt][4 * a4 + 3] * inv)};
-            *reinterpret_cast<bf16x4_t*>(op + 32 * (kDT * v + dt) + 8 * a4 + 4 * g) = o;
+            *reinterpret_cast<bf16x4_t*>(op + cb + 16 * dt + 8 * a4 + 4 * g + (a4 >= 2 ? 112 : 0)) = o;
           }
         }
         if (p.lse && v == 0 && g == 0) p.lse[(int64_t)(t0 + tk) * p.hq + hh] = lse2 * kLn2;
@@ -412,7 +418,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
           for (int a4 = 0; a4 < 4; ++a4) {
             const f32x4_t o = {oacc[dt][4 * a4] * inv, oacc[dt][4 * a4 + 1] * inv, oacc[dt][4 * a4 + 2] * inv,
                                oacc[dt][4 * a4 + 3] * inv};
-            *reinterpret_cast<f32x4_t*>(op + 32 * (kDT * v + dt) + 8 * a4 + 4 * g) = o;
+            *reinterpret_cast<f32x4_t*>(op + cb + 16 * dt + 8 * a4 + 4 * g + (a4 >= 2 ? 112 : 0)) = o;
           }
         }
         if (v == 0 && g == 0) p.part_lse[e] = lse2 == kNegInf ? kNegInf : lse2 * kLn2;

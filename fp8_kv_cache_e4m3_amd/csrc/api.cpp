@@ -220,8 +220,8 @@ struct DecodePlan {
 // The split grid takes 32-row tiles when a sequence has more than 16 rows per kv head and the head
 // dim is at most 256: each K/V unit is then loaded once for 32 rows instead of once per 16.  At
 // head dim 512 the two halves' O accumulators alone fill the 256 accumulation registers of a
-// decode wave (the kernel spilled in its loop, 5x slower), so 512 keeps 16-row tiles there; with
-// split Q, 32-row tiles at 512 run in the verify kernel, whose waves split the head dim of O.
+// decode wave (that kernel spilled in its loop, 5x slower), so 32-row tiles at 512 run in the
+// verify kernel, whose waves split the head dim of O.
 constexpr int32_t kBalancedMinUnits = 256;   // 4096 keys
 constexpr int32_t kMaxParts = 1 << 20;
 
@@ -258,7 +258,7 @@ DecodePlan plan_decode(const fp8attn_attn_args* a, int32_t requested) {
     pl.grid = R;
     return pl;
   }
-  if (rows > 16 && (a->head_dim <= 256 || (a->head_dim == 512 && a->q_dtype == FP8ATTN_BF16_SPLIT))) {
+  if (rows > 16) {
     pl.tile_rows = 32;
     pl.row_groups = (int32_t)((rows + 31) / 32);
     items = (int64_t)a->num_kv_heads * a->batch * pl.row_groups;
@@ -318,7 +318,7 @@ fp8attn_status run_decode(const char* fn, const fp8attn_attn_args* args, const D
     p.part_lse = reinterpret_cast<float*>(ws + round_up((size_t)pl.splits * rows * args->head_dim * sizeof(float)));
   }
   hipError_t e = pl.tile_rows == 32 && args->head_dim == 512
-                     ? fp8attn::launch_verify(p, pl.grid, stream)
+                     ? fp8attn::launch_verify(p, args->q_dtype == FP8ATTN_BF16_SPLIT, pl.grid, stream)
                      : fp8attn::launch_decode(p, args->q_dtype, args->head_dim, pl.grid, stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   if (pl.balanced) {

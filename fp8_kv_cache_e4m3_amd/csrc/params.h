@@ -88,10 +88,10 @@ hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, bool q_bf16, hi
 // block, 32-key tiles through LDS, both contractions on the MFMA.
 hipError_t launch_prefill_wide(const AttnParams& p, bool split_q, hipStream_t stream);
 
-// Decode with split Q (kQBf16Split) at head dim 512 over 32-row query tiles (p.tile_rows == 32):
-// the split grid's work items, one block each, K/V tiles through LDS shared by the 32 rows.
-// grid = row_groups * batch * S * hkv.
-hipError_t launch_verify(const AttnParams& p, int64_t grid, hipStream_t stream);
+// Decode with bf16 Q (q mode kQBf16, or kQBf16Split with split_q) at head dim 512 over 32-row query
+// tiles (p.tile_rows == 32): the split grid's work items, one block each, K/V tiles through LDS
+// shared by the 32 rows.  grid = row_groups * batch * S * hkv.
+hipError_t launch_verify(const AttnParams& p, bool split_q, int64_t grid, hipStream_t stream);
 
 hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t S, int64_t total_q,
                           int32_t hq, int32_t d, void* out, int64_t out_stride_tok,

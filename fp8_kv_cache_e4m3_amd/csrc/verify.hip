@@ -61,7 +61,8 @@ __device__ __forceinline__ float pow2i(float e) { return __builtin_amdgcn_ldexpf
 
 }  // namespace
 
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) verify_split_kernel(const AttnParams p) {
+template <bool SPLIT>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) verify_kernel(const AttnParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -186,12 +187,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     const int hq = h * G + (rvalid ? r : rlast) % G;
     const int pos = L - ql + tok;
 
-    // Q^T operands: per 128-d step c, lane (col, grp) holds hi and lo of Q[row][128 c + 32 grp .. + 31]
+    // Q^T operands.  Split: per 128-d step c, lane (col, grp) holds hi and lo of
+    // Q[row][128 c + 32 grp .. + 31].  BF16: per 32-d step c, lane (col, grp) holds Q[row][32 c + 8 grp .. + 7].
     const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)(t0 + tok) * p.q_stride_tok +
                        (int64_t)hq * p.q_stride_head;
-    i32x8_t qhi[4], qlo[4];
+    i32x8_t qhi[SPLIT ? 4 : 1], qlo[SPLIT ? 4 : 1];
+    bf16x8_t qb[SPLIT ? 1 : 16];
     float cs = p.scale_log2 * kd;
-    {
+    if constexpr (SPLIT) {
       u32x4_t raw[4][4];
       float amax = 0.f;
 #pragma unroll
@@ -223,41 +226,71 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
         qlo[c] = i32x8_t{(int)(uint32_t)lo[0], (int)(lo[0] >> 32), (int)(uint32_t)lo[1], (int)(lo[1] >> 32),
                          (int)(uint32_t)lo[2], (int)(lo[2] >> 32), (int)(uint32_t)lo[3], (int)(lo[3] >> 32)};
       }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const bf16x8_t z = {};
+        qb[c] = rvalid ? *reinterpret_cast<const bf16x8_t*>(qp + 32 * c + 8 * grp) : z;
+      }
     }
     // A operand of key block kb: MFMA row col holds key 16 kb + col; lane group grp takes d bytes
-    // 128 c + 32 grp .. + 31
-    const int k_lane = lane_offset(col * kRS + 32 * grp);
-    // this lane's P bytes: row n, lane group kb (keys 16 kb ..), bytes 4 grp .. (hi) and 16 + 4 grp .. (lo)
-    const int p_lane = lane_offset(n * kPRS + 4 * grp);
+    // 128 c + 32 grp .. + 31 (split) or 32 c + 8 grp .. + 7 (BF16)
+    const int k_lane = lane_offset(col * kRS + (SPLIT ? 32 : 8) * grp);
+    // this lane's P bytes in row n.  Split: lane group kb's 32 bytes (keys 16 kb ..), hi at 4 grp ..
+    // and lo at 16 + 4 grp ...  BF16: P of keys 16 kb + 4 grp .. + 3 as bf16, at byte 2 (16 kb + 4 grp).
+    const int p_lane = lane_offset(n * kPRS + (SPLIT ? 4 : 8) * grp);
 
-    // half (k-steps 2 hf, 2 hf + 1) of S^T of tile x, both 16-key blocks: every operand read first,
-    // then the MFMAs (two independent chains, one per key block)
+    // Half hf of S^T of tile x (the first or second half of the head dim), both 16-key blocks: every
+    // operand read first, then the MFMAs (two independent chains, one per key block).  Split: k-steps
+    // 2 hf, 2 hf + 1 of 128 d, K bytes as they are.  BF16: k-steps 8 hf .. 8 hf + 7 of 32 d, K bytes
+    // converted exactly to bf16.
     f32x4_t acc[2], done[2];
     auto qk_half = [&](int x, int hf) __attribute__((always_inline)) {
       const uint8_t* kst = sm_k + (x % kNSK) * kTile + k_lane;
-      i32x8_t kop[2][2];
+      if constexpr (SPLIT) {
+        i32x8_t kop[2][2];
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
+        for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const uint8_t* kp = kst + 16 * kb * kRS + 128 * (2 * hf + c2);
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kp);
-          const u32x4_t bb = *reinterpret_cast<const u32x4_t*>(kp + 16);
-          kop[c2][kb] = i32x8_t{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)bb[0], (int)bb[1], (int)bb[2], (int)bb[3]};
+          for (int kb = 0; kb < 2; ++kb) {
+            const uint8_t* kp = kst + 16 * kb * kRS + 128 * (2 * hf + c2);
+            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kp);
+            const u32x4_t bb = *reinterpret_cast<const u32x4_t*>(kp + 16);
+            kop[c2][kb] = i32x8_t{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)bb[0], (int)bb[1], (int)bb[2], (int)bb[3]};
+          }
         }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (hf == 0) {
-        acc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        acc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
+        __builtin_amdgcn_sched_barrier(0);
+        if (hf == 0) {
+          acc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          acc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const int c = 2 * hf + c2;
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const int c = 2 * hf + c2;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) acc[kb] = mfma_fp8_16x16x128(kop[c2][kb], qhi[c], acc[kb], kE8M0One);
+          for (int kb = 0; kb < 2; ++kb) acc[kb] = mfma_fp8_16x16x128(kop[c2][kb], qhi[c], acc[kb], kE8M0One);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) acc[kb] = mfma_fp8_16x16x128(kop[c2][kb], qlo[c], acc[kb], kE8M0Sixteenth);
+          for (int kb = 0; kb < 2; ++kb) acc[kb] = mfma_fp8_16x16x128(kop[c2][kb], qlo[c], acc[kb], kE8M0Sixteenth);
+        }
+      } else {
+        u32x2_t kraw[8][2];
+#pragma unroll
+        for (int c2 = 0; c2 < 8; ++c2) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            kraw[c2][kb] = *reinterpret_cast<const u32x2_t*>(kst + 16 * kb * kRS + 32 * (8 * hf + c2));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (hf == 0) {
+          acc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          acc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int c2 = 0; c2 < 8; ++c2) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            acc[kb] = mfma_bf16_16x16x32(e4m3x8_to_bf16(kraw[c2][kb][0], kraw[c2][kb][1]), qb[8 * hf + c2], acc[kb]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -304,12 +337,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
 #pragma unroll
         for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(sv[kb][i] - mb);
         lsum += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-        const uint32_t hi = pack4_e4m3(pv[0], pv[1], pv[2], pv[3]);
-        float back[4];
-        unpack4_e4m3(hi, back);
-        const uint32_t lo = pack4_e4m3(pv[0] - back[0], pv[1] - back[1], pv[2] - back[2], pv[3] - back[3]);
-        *reinterpret_cast<uint32_t*>(pb + 32 * kb) = hi;
-        *reinterpret_cast<uint32_t*>(pb + 32 * kb + 16) = lo;
+        if constexpr (SPLIT) {
+          const uint32_t hi = pack4_e4m3(pv[0], pv[1], pv[2], pv[3]);
+          float back[4];
+          unpack4_e4m3(hi, back);
+          const uint32_t lo = pack4_e4m3(pv[0] - back[0], pv[1] - back[1], pv[2] - back[2], pv[3] - back[3]);
+          *reinterpret_cast<uint32_t*>(pb + 32 * kb) = hi;
+          *reinterpret_cast<uint32_t*>(pb + 32 * kb + 16) = lo;
+        } else {
+          const bf16x4_t pw = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
+          *reinterpret_cast<bf16x4_t*>(pb + 32 * kb) = pw;
+        }
       }
       sm_l[x & 1][n][grp] = lsum;
       if (grp == 0) sm_m[x & 1][n] = m_run == kNegInf ? kNegInf : m_run - (8.0f - kLazyQK);
@@ -343,12 +381,25 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     // V^T transposing reads: this lane supplies key row 16 g + 8 o + (lane % 16) / 2 and 8-byte half
     // lane % 2 at column cb + 16 dt + 128 ((lane / 16) % 2); lane (n, g) receives O^T row n's column
     // of keys 16 g + 8 o .. + 7
-    const int v_lane = lane_offset((16 * g + ((lane & 15) >> 1)) * kRS + 128 * ((lane >> 4) & 1) + 8 * (lane & 1));
+    // (BF16: key rows 16 s + 8 g + (lane % 16) / 2 for k-step s)
+    const int v_lane = lane_offset(((SPLIT ? 16 : 8) * g + ((lane & 15) >> 1)) * kRS + 128 * ((lane >> 4) & 1) + 8 * (lane & 1));
 
     f32x16_t oacc[kDT];
 #pragma unroll
     for (int t = 0; t < kDT; ++t) oacc[t] = f32x16_t{};
     float m_ref = kNegInf, l_ref = 0.f;
+    // the common reference moves lazily, when a tile exceeds it by more than 2^16: O and l are
+    // rescaled by an exact power of two
+    auto rescale = [&](float m_t) __attribute__((always_inline)) {
+      const bool grow = m_t > m_ref + kSlack;
+      if (__any(grow)) {
+        const float alpha = grow && m_ref != kNegInf ? pow2i(m_ref - m_t) : 1.0f;
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt) oacc[dt] *= alpha;
+        l_ref *= alpha;
+        m_ref = grow ? m_t : m_ref;
+      }
+    };
 
     __syncthreads();
     for (int t = kt0 - 3; t <= kt1; ++t) {
@@ -356,34 +407,62 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
         // the tile's reference and partial sums for row n, then the common reference (moved lazily)
         const float m_t = sm_m[t & 1][n];
         const f32x4_t lp = *reinterpret_cast<const f32x4_t*>(&sm_l[t & 1][n][0]);
-        // P^T operand: lane group g's 32 bytes of row n (hi, then lo, of keys 16 g .. 16 g + 15)
-        const uint8_t* pb = sm_p + (t & 1) * kPBuf + n * kPRS + 32 * g;
-        const u32x4_t p0 = *reinterpret_cast<const u32x4_t*>(pb);
-        const u32x4_t p1 = *reinterpret_cast<const u32x4_t*>(pb + 16);
-        const i32x8_t pop = {(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3], (int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
-        // V^T operands: the 16 keys of lane group g, twice (against hi and lo)
+        const uint8_t* prow = sm_p + (t & 1) * kPBuf + n * kPRS;
         const uint8_t* vst = sm_v + (t % kNSV) * kTile + v_lane;
-        i32x8_t a[kDT];
+        if constexpr (SPLIT) {
+          // P^T operand: lane group g's 32 bytes of row n (hi, then lo, of keys 16 g .. 16 g + 15)
+          const u32x4_t p0 = *reinterpret_cast<const u32x4_t*>(prow + 32 * g);
+          const u32x4_t p1 = *reinterpret_cast<const u32x4_t*>(prow + 32 * g + 16);
+          const i32x8_t pop = {(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3], (int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
+          // V^T operands: the 16 keys of lane group g, twice (against hi and lo)
+          i32x8_t a[kDT];
 #pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) {
-          const i32x2_t v0 = lds_read_tr8(vst + cb + 16 * dt);
-          const i32x2_t v1 = lds_read_tr8(vst + 8 * kRS + cb + 16 * dt);
-          a[dt] = i32x8_t{v0[0], v0[1], v1[0], v1[1], v0[0], v0[1], v1[0], v1[1]};
+          for (int dt = 0; dt < kDT; ++dt) {
+            const i32x2_t v0 = lds_read_tr8(vst + cb + 16 * dt);
+            const i32x2_t v1 = lds_read_tr8(vst + 8 * kRS + cb + 16 * dt);
+            a[dt] = i32x8_t{v0[0], v0[1], v1[0], v1[1], v0[0], v0[1], v1[0], v1[1]};
+          }
+          rescale(m_t);
+          // E8M0 scale of the tile for this row: 2^(m_t - m_ref) (at most 2^16; a masked tile: 0)
+          const int code = m_t == kNegInf ? 0 : 127 + (int)fmaxf(m_t - m_ref, -127.0f);
+          if (m_t != kNegInf) l_ref += ((lp[0] + lp[1]) + (lp[2] + lp[3])) * pow2i(m_t - m_ref);
+#pragma unroll
+          for (int dt = 0; dt < kDT; ++dt)
+            oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[dt], pop, oacc[dt], 0, 0, 0, kE8M0One, 0, code);
+        } else {
+          // P^T operands of k-steps s = 0, 1: row n's bf16 P of keys 16 s + 8 g .. + 7, brought from the
+          // tile's reference to the common one (an exact power of two)
+          bf16x8_t pop[2];
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) pop[s2] = *reinterpret_cast<const bf16x8_t*>(prow + 32 * s2 + 16 * g);
+          // V^T operands: keys 16 s + 8 g .. + 7 of the lane's column, converted exactly to bf16
+          u32x2_t vraw[kDT][2];
+#pragma unroll
+          for (int dt = 0; dt < kDT; ++dt) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+              const i32x2_t v2 = lds_read_tr8(vst + 16 * s2 * kRS + cb + 16 * dt);
+              vraw[dt][s2] = u32x2_t{(uint32_t)v2[0], (uint32_t)v2[1]};
+            }
+          }
+          rescale(m_t);
+          if (m_t != kNegInf) l_ref += ((lp[0] + lp[1]) + (lp[2] + lp[3])) * pow2i(m_t - m_ref);
+          const float sc = m_t == kNegInf ? 0.f : pow2i(m_t - m_ref);
+          if (!__all(sc == 1.0f)) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+              for (int i = 0; i < 8; ++i) pop[s2][i] = (__bf16)((float)pop[s2][i] * sc);
+            }
+          }
+#pragma unroll
+          for (int dt = 0; dt < kDT; ++dt) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+              oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16(vraw[dt][s2][0], vraw[dt][s2][1]),
+                                                                 pop[s2], oacc[dt], 0, 0, 0);
+          }
         }
-        const bool grow = m_t > m_ref + kSlack;
-        if (__any(grow)) {
-          const float alpha = grow && m_ref != kNegInf ? pow2i(m_ref - m_t) : 1.0f;
-#pragma unroll
-          for (int dt = 0; dt < kDT; ++dt) oacc[dt] *= alpha;
-          l_ref *= alpha;
-          m_ref = grow ? m_t : m_ref;
-        }
-        // E8M0 scale of the tile for this row: 2^(m_t - m_ref) (at most 2^16; a masked tile: 0)
-        const int code = m_t == kNegInf ? 0 : 127 + (int)fmaxf(m_t - m_ref, -127.0f);
-        if (m_t != kNegInf) l_ref += ((lp[0] + lp[1]) + (lp[2] + lp[3])) * pow2i(m_t - m_ref);
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt)
-          oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[dt], pop, oacc[dt], 0, 0, 0, kE8M0One, 0, code);
       }
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
@@ -427,9 +506,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   }
 }
 
-hipError_t launch_verify(const AttnParams& p, int64_t grid, hipStream_t stream) {
+hipError_t launch_verify(const AttnParams& p, bool split_q, int64_t grid, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(verify_split_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  if (split_q) hipLaunchKernelGGL(verify_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  else hipLaunchKernelGGL(verify_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

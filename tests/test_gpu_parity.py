@@ -357,7 +357,7 @@ def test_split_q(d, entry, splits):
     o, l, _, s = gpu_run(w, entry, num_splits=splits, split_q=True)
     compare(o, o_ref, l, l_ref, label=f"split-q d{d} {entry} S={s}")
     o_b, l_b, _, s_b = gpu_run(w, entry, num_splits=splits)
-    assert s_b == s or splits == 0   # (automatic plans: split Q at d512 runs 32-row tiles)
+    assert s_b == s
     assert np.max(np.abs(o - o_b)) <= 1.6e-2 and np.max(np.abs(l - l_b)) <= 1e-4, \
         (np.max(np.abs(o - o_b)), np.max(np.abs(l - l_b)))
 

@@ -1,12 +1,14 @@
-// Multi-token decode at head dim 512 with split Q on the FP8 MFMA: steps with 17-32 query rows per
+// Multi-token decode at head dim 512 with bf16 queries: steps with more than 16 query rows per
 // (sequence, kv head), such as speculative-decode verification, where GQA 8 times 4 tokens (the
 // target token and three drafts) meet one long cached context (vLLM PR #60372, Validation: MTP with
 // three speculative tokens over a shared prefix; Overview: the full-attention layers at head dim 512
 // keep BF16 queries; review thread: the d512 FP8-MMA kernel with its split QK accumulation).
 //
-// What it computes: the same masked softmax attention as the decode kernel's split-Q mode (bf16 Q
-// written per row as 2^-e (hi + lo / 16) in E4M3, exact for bf16 values; QK^T and PV on the FP8
-// MFMA; P as two E4M3 terms), for a tile of 32 query rows, over one split of the key range.
+// What it computes: the masked softmax attention of the decode kernel's two bf16-Q modes, for a
+// tile of 32 query rows over one split of the key range:
+//   SPLIT = true (q_dtype BF16_SPLIT): Q per row as 2^-e (hi + lo / 16) in E4M3 (exact for bf16
+//     values), QK^T and PV on the FP8 MFMA, P as two E4M3 terms;
+//   SPLIT = false (q_dtype BF16): K and V converted exactly to bf16, BF16 MFMAs, P rounded to bf16.
 //
 // Design (gfx950, wave64, 640 threads = 10 waves, one block per compute unit):
 //  * Every K/V byte of the tile's key range is loaded once for all 32 rows: 32-key tiles go from
@@ -15,22 +17,24 @@
 //    bytes (a copy of the row's first 16 bytes), which makes the operand reads conflict-free.
 //  * Three roles.  Two loader waves (8: K, 9: V) only issue the tile loads, so no computing wave
 //    ever stalls on a full load queue.  Four QK waves: wave (parity, row half) computes S^T = K Q^T
-//    for the 16 rows of its half and all 32 keys of every other tile on the scaled 16x16x128 MFMA
-//    (the lo terms of Q at operand scale 2^-4), half the head dim in each of two intervals, then
-//    that tile's softmax in the next interval while the MFMAs of its next tile run.  Four PV waves
-//    each own 128 of the 512 head-dim columns of O for all 32 rows and run O^T += V^T P^T on the
-//    scaled 32x32x64 MFMA.  One barrier per tile; tile x: QK^T in intervals x - 3 and x - 2,
-//    softmax in x - 1, PV in x.
+//    for the 16 rows of its half and all 32 keys of every other tile (scaled 16x16x128 FP8 MFMA
+//    with the lo terms of Q at operand scale 2^-4, or 16x16x32 BF16), half the head dim in each of
+//    two intervals, then that tile's softmax in the next interval while the MFMAs of its next tile
+//    run.  Four PV waves each own 128 of the 512 head-dim columns of O for all 32 rows and run
+//    O^T += V^T P^T (scaled 32x32x64 FP8, or 32x32x16 BF16).  One barrier per tile; tile x: QK^T
+//    in intervals x - 3 and x - 2, softmax in x - 1, PV in x.
 //  * No running maximum is shared between waves.  A QK wave keeps, per row, an integer reference
 //    m that moves lazily (when the tile exceeds it by more than 2, to the ceiling of the tile's
 //    row maximum: the only cross-lane reduction, rare after the first tiles), so that
 //    P = 2^(s - m + 6) <= 2^8, and it publishes m - 6 with P and its lanes' partial row sums.  The
-//    PV MFMA's per-lane E8M0 operand scale brings each tile to the PV waves' common reference
-//    exactly: on gfx950 the B scale of lane n + 32 kb covers bytes 16 kb .. 16 kb + 15 of both
-//    lane groups of column n.  Lane group g holds hi = E4M3(P) of keys 16 g .. 16 g + 15 in bytes
-//    0-15 (scale block 0) and lo = E4M3(P - hi) of the same keys in bytes 16-31 (scale block 1),
-//    against the same V bytes twice in A; both blocks carry the tile's scale for row n.  The PV
-//    reference moves lazily too (by more than 2^16), with an O rescale by an exact power of two.
+//    PV waves bring each tile from its reference to their common one by an exact power of two.
+//    With split Q that is the PV MFMA's per-lane E8M0 operand scale: on gfx950 the B scale of lane
+//    n + 32 kb covers bytes 16 kb .. 16 kb + 15 of both lane groups of column n.  Lane group g
+//    holds hi = E4M3(P) of keys 16 g .. 16 g + 15 in bytes 0-15 (scale block 0) and lo =
+//    E4M3(P - hi) of the same keys in bytes 16-31 (scale block 1), against the same V bytes twice
+//    in A; both blocks carry the tile's scale for row n.  With BF16 Q the PV waves multiply the
+//    bf16 P by it.  The common reference moves lazily too (by more than 2^16), with an O rescale
+//    by an exact power of two.
 #include "device.h"
 #include "params.h"
 

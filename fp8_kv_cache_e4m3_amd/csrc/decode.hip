@@ -22,8 +22,8 @@
 //  * Work item = (kv head, split, sequence, row tile), XCD-aware block order, or a range of the
 //    balanced partition (decode_balanced_kernel).  4 waves per block; each wave streams its own
 //    16-key units (a quarter of the range) straight from HBM into registers, with the next
-//    unit's loads in flight while the current one is computed.  No LDS staging and no barriers
-//    in the main loop.
+//    unit's loads in flight while the current one is computed.  No barriers in the main loop;
+//    K passes through a wave-private LDS tile to turn its row-order loads into MFMA operands.
 //  * S^T = K * Q^T: the 16 keys are MFMA rows, the 16 query rows are MFMA columns, so every
 //    query row lives on one lane column (lane % 16) and its softmax state is per lane.
 //  * O^T = V^T * P^T: P^T comes straight out of the S^T accumulator layout (lane (r, g) holds
@@ -61,6 +61,9 @@ struct DecodeShape {
   static constexpr int VBLK = D / (16 * CW);          // V column blocks
   static constexpr int NT = D / 16;                   // O^T tiles (16 d-rows each)
   static constexpr int RS = D + 4;                    // LDS row stride (floats), padded
+  static constexpr bool KROW = D <= 256;              // K loaded in row order (see UnitOffsets)
+  static constexpr int KTS = D + 16;                  // K tile row stride (bytes), padded
+  static constexpr int KOFS = KROW && 1024 % D != 0 ? KCH : 1;   // per-lane K load offsets kept
   static_assert(D == 64 || D == 128 || D == 192 || D == 256 || D == 512, "head dim");
 };
 
@@ -80,8 +83,8 @@ __device__ __forceinline__ rsrc_t unit_rsrc(const uint8_t* base, uint32_t num_re
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)num_records, 0x00020000);
 }
 template <bool NT>
-__device__ __forceinline__ u32x4_t stream_load16(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0);
+__device__ __forceinline__ u32x4_t stream_load16(rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, NT ? 2 : 0);
 }
 template <bool NT>
 __device__ __forceinline__ u32x2_t stream_load8(rsrc_t r, uint32_t off) {
@@ -92,27 +95,93 @@ __device__ __forceinline__ uint32_t stream_load4(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, NT ? 2 : 0);
 }
 
-// Per-lane byte offsets inside a unit, the same for every unit: K row col, bytes 16 grp (+ 64 c);
-// V rows 4 grp + i, bytes col * CW (+ 16 CW blk).  A unit's loads are then a uniform base (page
-// plus first slot) plus these 32-bit offsets: the SGPR-base form of the global loads.
+// Per-lane byte offsets inside a unit, the same for every unit.  A unit's loads are a uniform
+// base (page plus first slot) plus these 32-bit offsets: the SGPR-base form of the global loads.
+//  * K is read in row order: load c covers bytes [1024 c, 1024 c + 1024) of the unit's 16 x D
+//    bytes taken row by row, lane l the 16 bytes at 16 (64 c + l), so each 16-lane quarter of a
+//    load reads whole 256-byte runs of one or more key rows.  (The MFMA operand layout read
+//    straight from memory, lane (col, grp) taking bytes 16 grp + 64 c of key col, has every
+//    quarter touch 16 rows: a plain gather with that pattern is 7% slower on the sliding-window
+//    decode's K/V stream.)  The operand layout then comes out of a wave-private LDS tile
+//    (k_operands).  Load c's offset is k[0] + c kstep (1024 / D rows per load), or k[c] (head
+//    dim 192, whose rows straddle the loads).  Head dim 512 keeps the operand layout in its loads
+//    (k[0] + 64 c): its rows already fill two quarters each way, and the LDS round trip measured
+//    0.6% slower on the full-attention decode.
+//  * V rows 4 grp + i, bytes col * CW (+ 16 CW blk): each quarter reads whole rows already.
+template <int D>
 struct UnitOffsets {
-  uint32_t k;
+  uint32_t k[DecodeShape<D>::KOFS];
+  uint32_t kstep;
   uint32_t v[4];
 };
 
+// position of lane l's K bytes of load c in the unit's row-major 16 x D bytes
+template <int D>
+__device__ __forceinline__ int k_row(int c, int lane) { return (16 * (64 * c + lane)) / D; }
+template <int D>
+__device__ __forceinline__ int k_col(int c, int lane) { return (16 * (64 * c + lane)) % D; }
+
+template <int D>
+__device__ __forceinline__ UnitOffsets<D> unit_offsets(const int64_t sT, const int lane) {
+  using S = DecodeShape<D>;
+  const int col = lane & 15, grp = lane >> 4;
+  UnitOffsets<D> o;
+  if constexpr (S::KROW) {
+#pragma unroll
+    for (int c = 0; c < S::KOFS; ++c) o.k[c] = (uint32_t)(k_row<D>(c, lane) * sT) + (uint32_t)k_col<D>(c, lane);
+    o.kstep = (uint32_t)((1024 / D) * sT);
+  } else {
+    o.k[0] = (uint32_t)(col * sT) + 16u * (uint32_t)grp;
+    o.kstep = 64u;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o.v[i] = (uint32_t)((4 * grp + i) * sT) + (uint32_t)(col * S::CW);
+  return o;
+}
+
+// K of a unit from the row order of the loads to the MFMA A-operand layout (lane (col, grp):
+// key col, bytes 16 grp + 64 c of chunk c) through the wave's LDS tile of 16 rows x KTS bytes.
+// The padded row stride puts the 16 rows that one read quarter touches in distinct banks.  The
+// tile is the wave's own: its accesses are ordered by the wave's program order, no barrier.
+template <int D>
+__device__ __forceinline__ void k_operands(const u32x4_t (&in)[DecodeShape<D>::KCH],
+                                           u32x4_t (&out)[DecodeShape<D>::KCH], uint8_t* kt, const int lane) {
+  using S = DecodeShape<D>;
+  if constexpr (!S::KROW) {
+#pragma unroll
+    for (int c = 0; c < S::KCH; ++c) out[c] = in[c];
+    return;
+  }
+#pragma unroll
+  for (int c = 0; c < S::KCH; ++c)
+    *reinterpret_cast<u32x4_t*>(kt + k_row<D>(c, lane) * S::KTS + k_col<D>(c, lane)) = in[c];
+  const uint8_t* rd = kt + (lane & 15) * S::KTS + 16 * (lane >> 4);
+#pragma unroll
+  for (int c = 0; c < S::KCH; ++c) out[c] = *reinterpret_cast<const u32x4_t*>(rd + 64 * c);
+}
+
 // D: the register layout's head dim; DV < D (head dim 96 in a 128 layout): the lanes whose
-// bytes lie past DV (k_hi_ok false: the last K chunk; v_ok false: the V columns) load nothing
-// and hold zeros, so no byte outside the head is read and the padding adds nothing.
+// bytes lie past DV (k_ok false: the K bytes, at the same columns in every load; v_ok false:
+// the V columns) load nothing and hold zeros, so no byte outside the head is read and the
+// padding adds nothing.  trailing: the unit is a filler load past the stream's end (see issue in
+// decode_tile): every lane reads the unit's first 16 bytes.
 template <int D, int DV, bool NT>
 __device__ __forceinline__ void load_unit(UnitRegs<D>& ur, const rsrc_t kunit, const rsrc_t vunit,
-                                          const UnitOffsets& off, const bool k_hi_ok, const bool v_ok) {
+                                          const UnitOffsets<D>& off, const bool k_ok, const bool v_ok,
+                                          const bool trailing) {
   using S = DecodeShape<D>;
+  static_assert(DV == D || (S::KROW && S::KOFS == 1), "a padded head dim needs the same K columns in every load");
+  const uint32_t kstep = trailing ? 0u : off.kstep;
 #pragma unroll
   for (int c = 0; c < S::KCH; ++c) {
-    if (DV == D || c < S::KCH - 1 || k_hi_ok)
-      ur.k[c] = stream_load16<NT>(kunit, off.k + 64 * c);
-    else
+    if (DV == D || k_ok) {
+      if constexpr (S::KOFS == 1)
+        ur.k[c] = stream_load16<NT>(kunit, trailing ? 0u : off.k[0], c * kstep);
+      else
+        ur.k[c] = stream_load16<NT>(kunit, trailing ? 0u : off.k[c]);
+    } else {
       ur.k[c] = u32x4_t{0, 0, 0, 0};
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -144,10 +213,10 @@ __device__ __forceinline__ void load_unit(UnitRegs<D>& ur, const rsrc_t kunit, c
 
 // Per-variant tuning (measured on MI355X, sliding-window decode, cold K/V).  Two units in
 // flight per wave; deeper register rings (3 or 4 units, which fit at two waves per SIMD) were
-// slower, as were rings staged through LDS with direct-to-LDS loads.  A plain gather with this
-// access pattern (256-byte row slices, 16 rows per instruction) tops out near 47 us for the
-// 269 MB, against about 50 us for the kernel.  Non-temporal loads help the d256 stream (+4%)
-// and hurt the split d512 stream (-11%).
+// slower, as were rings staged through LDS with direct-to-LDS loads.  A plain gather of the
+// same 269 MB in the same order (whole 256-byte row slices per 16-lane quarter, 4 waves x 512
+// blocks) takes 41.9 us; the kernel about 45.7 us.  Non-temporal loads help the d256 stream
+// (+4%) and hurt the split d512 stream (-11%).
 template <bool QFP8, int D>
 struct DecodeTune {
   static constexpr int NBUF = 2;
@@ -331,13 +400,10 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
     return __builtin_amdgcn_readlane(pg_vec, pi - pg_base);
   };
 
-  // (head dim 96 in the 128 layout: this lane's last K chunk, and its V columns, lie in the head)
-  const bool k_hi_ok = 64 * (S::KCH - 1) + 16 * grp < D;
+  // (head dim 96 in the 128 layout: this lane's K bytes, and its V columns, lie in the head)
+  const bool k_ok = !S::KROW || k_col<DP>(0, lane) < D;
   const bool v_ok = col * S::CW < D;
-  UnitOffsets uoff;
-  uoff.k = (uint32_t)(col * sT) + 16u * (uint32_t)grp;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) uoff.v[i] = (uint32_t)((4 * grp + i) * sT) + (uint32_t)(col * S::CW);
+  const UnitOffsets<DP> uoff = unit_offsets<DP>(sT, lane);
   // Loads past the split's last unit keep the number of loads per trip fixed, so that the
   // compiler waits for exactly the oldest unit.  They read the last unit's first 16 bytes in every
   // lane: one cache line, which costs next to nothing and lands quickly at the end of the stream.
@@ -348,11 +414,11 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
     const int64_t unit = page_of(uc) * sP + (int64_t)((uc * 16) % ps) * sT;
     // the unit's keys below L (at least one: uc * 16 <= p_last < L)
     const uint32_t nrec = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(16, L - uc * 16))) * (uint32_t)sT;
-    UnitOffsets o = uoff;
-    o.k = trailing ? 0u : o.k;
+    UnitOffsets<DP> o = uoff;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o.v[i] = trailing ? 0u : o.v[i];
-    load_unit<DP, D, T::NT>(ur, unit_rsrc(kbase + unit, nrec), unit_rsrc(vbase + unit, nrec), o, k_hi_ok, v_ok);
+    load_unit<DP, D, T::NT>(ur, unit_rsrc(kbase + unit, nrec), unit_rsrc(vbase + unit, nrec), o, k_ok, v_ok,
+                            trailing);
   };
 
   // S^T tile of a unit: rows = its 16 keys, columns = the 16 query rows
@@ -450,8 +516,14 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
   // One 16x16x32 MFMA per O^T tile takes the lane's 4 keys twice, 16 hi in byte slots 0-3 and
   // lo in slots 4-7, against the same 4 V bytes in both halves of the A operand, so it
   // accumulates 16 O; the 1/16 goes into the final 1/l.
+  // the wave's K tile: the first bytes of its O slot in the merge buffer, which it writes only
+  // after the barrier that ends every wave's stream
+  uint8_t* ktile = reinterpret_cast<uint8_t*>(&sm_o[wave][0][0]);
+  static_assert(sizeof(sm_o[0]) >= 16 * S::KTS, "K tile");
   auto compute = [&](const UnitRegs<DP>& ur, int u) __attribute__((always_inline)) {
-    const f32x4_t pf = softmax(qk(ur.k), u);
+    u32x4_t kk[S::KCH];
+    k_operands<DP>(ur.k, kk, ktile, lane);
+    const f32x4_t pf = softmax(qk(kk), u);
     uint64_t p8 = 0;
     bf16x4_t pb = {};
     if constexpr (SPLIT) {
@@ -661,7 +733,8 @@ __device__ __forceinline__ void decode_tile32(const AttnParams& p, const int b, 
   constexpr int QIMG = 2 * NQ * 64 * QB;              // image [half][operand][lane] (split Q: hi)
   constexpr int QLDS = SPLIT ? 2 * QIMG : QIMG;       // (split Q: the lo image follows)
   constexpr int MERGE = 4 * 16 * S::RS * 4;           // one half's O of the 4 waves, fp32
-  __shared__ __attribute__((aligned(16))) uint8_t smem[QLDS > MERGE ? QLDS : MERGE];
+  constexpr int KT = QLDS + 4 * 16 * S::KTS;         // Q image, then the 4 waves' K tiles
+  __shared__ __attribute__((aligned(16))) uint8_t smem[KT > MERGE ? KT : MERGE];
   __shared__ float sm_m[4][16];
   __shared__ float sm_l[4][16];
   __shared__ float sm_cs[32];
@@ -740,23 +813,20 @@ __device__ __forceinline__ void decode_tile32(const AttnParams& p, const int b, 
     }
     return __builtin_amdgcn_readlane(pg_vec, pi - pg_base);
   };
-  const bool k_hi_ok = 64 * (S::KCH - 1) + 16 * grp < D;
+  const bool k_ok = !S::KROW || k_col<DP>(0, lane) < D;
   const bool v_ok = col * S::CW < D;
-  UnitOffsets uoff;
-  uoff.k = (uint32_t)(col * sT) + 16u * (uint32_t)grp;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) uoff.v[i] = (uint32_t)((4 * grp + i) * sT) + (uint32_t)(col * S::CW);
+  const UnitOffsets<DP> uoff = unit_offsets<DP>(sT, lane);
   const int ulast = su1 - 1;
   auto issue = [&](UnitRegs<DP>& ur, int u) __attribute__((always_inline)) {
     const bool trailing = u > ulast;
     const int uc = trailing ? ulast : u;
     const int64_t unit = page_of(uc) * sP + (int64_t)((uc * 16) % ps) * sT;
     const uint32_t nrec = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(16, L - uc * 16))) * (uint32_t)sT;
-    UnitOffsets o = uoff;
-    o.k = trailing ? 0u : o.k;
+    UnitOffsets<DP> o = uoff;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o.v[i] = trailing ? 0u : o.v[i];
-    load_unit<DP, D, T::NT>(ur, unit_rsrc(kbase + unit, nrec), unit_rsrc(vbase + unit, nrec), o, k_hi_ok, v_ok);
+    load_unit<DP, D, T::NT>(ur, unit_rsrc(kbase + unit, nrec), unit_rsrc(vbase + unit, nrec), o, k_ok, v_ok,
+                            trailing);
   };
 
   // the first units' loads go out before Q is staged, so their latencies overlap
@@ -925,9 +995,12 @@ __device__ __forceinline__ void decode_tile32(const AttnParams& p, const int b, 
   };
 
   // O^T += V^T * P^T for both halves; the V^T operands (byte transpose, dequant) are made once
+  uint8_t* ktile = smem + QLDS + wave * 16 * S::KTS;   // the wave's K tile, after the Q image
   auto compute = [&](const UnitRegs<DP>& ur, int u) __attribute__((always_inline)) {
     f32x4_t sacc[2];
-    qk(ur.k, sacc);
+    u32x4_t kk[S::KCH];
+    k_operands<DP>(ur.k, kk, ktile, lane);
+    qk(kk, sacc);
     uint64_t p8[2] = {0, 0};
     bf16x4_t pb[2] = {};
 #pragma unroll

@@ -216,7 +216,8 @@ __device__ __forceinline__ void load_unit(UnitRegs<D>& ur, const rsrc_t kunit, c
 // slower, as were rings staged through LDS with direct-to-LDS loads.  A plain gather of the
 // same 269 MB in the same order (whole 256-byte row slices per 16-lane quarter, 4 waves x 512
 // blocks) takes 41.9 us; the kernel about 45.7 us.  Non-temporal loads help the d256 stream
-// (+4%) and hurt the split d512 stream (-11%).
+// (+4%) and the balanced partition at d512 (full-attention decode 908 -> 853 us); on the split
+// grid at d512 they measured 11% slower (they are set per launch shape in decode_tile).
 template <bool QFP8, int D>
 struct DecodeTune {
   static constexpr int NBUF = 2;
@@ -417,7 +418,7 @@ __device__ __forceinline__ void decode_tile(const AttnParams& p, const int b, co
     UnitOffsets<DP> o = uoff;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o.v[i] = trailing ? 0u : o.v[i];
-    load_unit<DP, D, T::NT>(ur, unit_rsrc(kbase + unit, nrec), unit_rsrc(vbase + unit, nrec), o, k_ok, v_ok,
+    load_unit<DP, D, T::NT || (BAL && DP == 512)>(ur, unit_rsrc(kbase + unit, nrec), unit_rsrc(vbase + unit, nrec), o, k_ok, v_ok,
                             trailing);
   };
 

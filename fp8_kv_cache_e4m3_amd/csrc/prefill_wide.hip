@@ -435,8 +435,9 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2
     const int rr = wr0 + row;
     if (rr < nrows) {
       const int tk = rr / G, hh = h * G + rr % G;
-      *reinterpret_cast<u32x4_t*>(obase + (int64_t)(t0 + tk) * p.out_stride_tok + (int64_t)hh * p.out_stride_head +
-                                  8 * cc) = v;
+      // (non-temporal: O is written once)
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(obase + (int64_t)(t0 + tk) * p.out_stride_tok +
+                                                                (int64_t)hh * p.out_stride_head + 8 * cc));
     }
   }
   if (p.lse && grp == 0 && rvalid)

@@ -43,7 +43,9 @@ __global__ void __launch_bounds__(256) cache_write_kernel(const CacheWriteParams
   const int64_t pos = slot - page * p.page_size;
   uint8_t* dst = (which ? p.v_cache : p.k_cache) + page * p.kv_stride_page + pos * p.kv_stride_tok +
                  (int64_t)head * p.kv_stride_head + 16 * chunk;
-  *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{c0[0], c0[1], c1[0], c1[1]};
+  // (a non-temporal store: 2% faster on the sliding-window prefill's 65,536 tokens than a plain
+  // one; non-temporal loads, or two chunks per thread, measured no better)
+  __builtin_nontemporal_store(u32x4_t{c0[0], c0[1], c1[0], c1[1]}, reinterpret_cast<u32x4_t*>(dst));
 }
 
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream) {

@@ -236,6 +236,7 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
 #pragma unroll
   for (int t = 0; t < S::NDT; ++t) oacc[t] = f32x16_t{};
   float m_used = kNegInf, l_run = 0.f;
+  float l_q = 0.f;   // single P: the sum of the E4M3 P values (the normalization of O)
   f32x16_t sacc[2];                 // S^T of the tile being processed (two 32-key halves)
   i32x8_t pb = {}, pbl = {};        // P^T operands (hi and, for SPLIT, lo) of that tile
 
@@ -332,6 +333,7 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
       const float alpha = fast_exp2(m_used - (m_new == kNegInf ? 0.f : m_new));
       if (grow) {
         l_run *= alpha;
+        if constexpr (!SPLIT) l_q *= alpha;
         m_used = m_new;
       }
       const float a = grow ? alpha : 1.0f;
@@ -339,8 +341,14 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
       for (int t = 0; t < S::NDT; ++t) oacc[t] *= a;
     }
     const float neg_m = m_used == kNegInf ? 0.f : -m_used;
-    // P = exp2(s * cs - m), packed to E4M3 in the B-operand slot order (slot 16*h2 + i)
-    float lsum = 0.f;
+    // P = exp2(s * cs - m), packed to E4M3 in the B-operand slot order (slot 16*h2 + i).  The
+    // single-P instance normalizes O by the sum of the E4M3 values the PV MFMA takes, so that the
+    // weights of a row sum to 1 exactly: with the unrounded sum, a row whose attention sits on a
+    // few keys carried their rounding error straight into O (on the sliding-window prefill's 2M
+    // rows the worst row erred by 0.036 against the exact softmax, 0.028 with this sum, for about
+    // 1% more time).  The LSE keeps the unrounded sum.  The split-P instance's hi + lo / 16 is
+    // within the unrounded sum's rounding.
+    float lsum = 0.f, lqsum = 0.f;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
@@ -353,6 +361,11 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
         }
         const uint32_t hi = pack4_e4m3(e[0], e[1], e[2], e[3]);
         pb[4 * h2 + q4] = (int)hi;
+        if constexpr (!SPLIT) {
+          float r4[4];
+          unpack4_e4m3(hi, r4);
+          lqsum += (r4[0] + r4[1]) + (r4[2] + r4[3]);
+        }
         if constexpr (SPLIT) {
           float back[4], rsd[4];
           unpack4_e4m3(hi, back);
@@ -363,9 +376,10 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
       }
     }
     l_run += lsum;
+    if constexpr (!SPLIT) l_q += lqsum;
     // P and the running sum are needed right here: without this the compiler sinks the whole
     // exponential block past the barrier that follows, into the MFMA half of the period.
-    asm volatile("" ::"v"(pb), "v"(l_run));
+    asm volatile("" ::"v"(pb), "v"(l_run), "v"(l_q));
     if constexpr (SPLIT) asm volatile("" ::"v"(pbl));
   };
 
@@ -484,7 +498,9 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   // (the first few hundred rows of each sequence) keeps the direct stores: it has no registers
   // to spare for the staging.
   l_run += __shfl_xor(l_run, 32, 64);
-  const float inv = l_run > 0.f ? vd / l_run : 0.f;
+  if constexpr (!SPLIT) l_q += __shfl_xor(l_q, 32, 64);
+  const float l_norm = SPLIT ? l_run : l_q;
+  const float inv = l_norm > 0.f ? vd / l_norm : 0.f;
   if constexpr (!SPLIT) {
     constexpr int ORS = 2 * D + 16;                 // LDS row stride of the staged O (bytes)
     static_assert(S::NW * S::RW * ORS <= 4 * SB, "the staged O fits the stage ring");

@@ -190,18 +190,31 @@ __device__ __forceinline__ f32x4_t mfma_fp8_16x16x32(uint64_t a, uint64_t b, f32
 // ---------------------------------------------------------------------------------------------
 // Cross-lane helpers (wave64)
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
-  return __shfl_xor(v, mask, 64);
+// gfx950's lane-swap instructions exchange 16-lane rows (v_permlane16_swap: rows 0<->1 and 2<->3)
+// or 32-lane halves (v_permlane32_swap) between two registers on the VALU, without the LDS round
+// trip of a ds_bpermute.  Given the value twice, the two results hold, in every lane, the lane's
+// own value and its partner's (lane l ^ 16, or l ^ 32), in an order that depends on the lane;
+// max and sum of the pair are symmetric, so every lane gets the pair's max or sum (bit-identical
+// to v + shfl(v), since fp32 addition commutes).
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 // reduce over the four 16-lane groups (lanes l, l^16, l^32, l^48)
-__device__ __forceinline__ float max_over_groups(float v) {
-  v = fmaxf(v, shfl_xor_f(v, 16));
-  return fmaxf(v, shfl_xor_f(v, 32));
-}
-__device__ __forceinline__ float sum_over_groups(float v) {
-  v += shfl_xor_f(v, 16);
-  return v + shfl_xor_f(v, 32);
-}
+__device__ __forceinline__ float max_over_groups(float v) { return max_xor32(max_xor16(v)); }
+__device__ __forceinline__ float sum_over_groups(float v) { return sum_xor32(sum_xor16(v)); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

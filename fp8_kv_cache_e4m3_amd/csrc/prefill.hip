@@ -324,7 +324,7 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
 #pragma unroll
       for (int i = 0; i < 16; ++i) mxr = fmaxf(mxr, sacc[h2][i]);
     }
-    mxr = fmaxf(mxr, __shfl_xor(mxr, 32, 64));
+    mxr = max_xor32(mxr);
     const float mx = mxr * cs;
     // lazy maximum: move it only when the tile exceeds it by more than 2^8
     const bool grow = mx > m_used + kLazyMax;
@@ -497,8 +497,8 @@ __global__ void __launch_bounds__(512) prefill_fp8_kernel(const AttnParams p, in
   // into each of 32 rows, and HBM took a third more bytes than O has.  The split-P instance
   // (the first few hundred rows of each sequence) keeps the direct stores: it has no registers
   // to spare for the staging.
-  l_run += __shfl_xor(l_run, 32, 64);
-  if constexpr (!SPLIT) l_q += __shfl_xor(l_q, 32, 64);
+  l_run = sum_xor32(l_run);
+  if constexpr (!SPLIT) l_q = sum_xor32(l_q);
   const float l_norm = SPLIT ? l_run : l_q;
   const float inv = l_norm > 0.f ? vd / l_norm : 0.f;
   if constexpr (!SPLIT) {
